@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the multi-head attention forward pass.
+
+This module is shared by the fp64 oracle's tests, the GPU parity tests, the
+benchmark and the smoke check. It holds workload descriptions and random
+draws only: none of the attention arithmetic lives here.
+
+Workloads follow the pages' own settings where they give them:
+
+* d_model = 512, h = 8, d_k = d_v = 64 is the original paper's setting quoted
+  by itwiki "멀티 헤드 어텐션", section 수식, and by molayo1419.me
+  "MHA란 무엇인가?", closing references.
+* Batch-first (B, T, D) inputs, as in the tensor-shape table of itwiki
+  "멀티 헤드 어텐션", section 텐서 모양으로 본 계산.
+* Cross-attention takes queries from one sequence and keys/values from
+  another (itwiki, section 수식, last paragraph; iamjaehka13.blog
+  "[Deep Learning 5] Attention의 내부 계산", §19).
+* A key-padding mask marks keys to IGNORE with a nonzero value, the
+  nn.MultiheadAttention convention described in molayo1419.me, trap 2.
+
+Readings taken where the workload text is silent (each is listed in the
+design notes):
+
+* "Xavier-uniform" is U(-a, a), a = sqrt(6 / (fan_in + fan_out)), gain 1.
+  For the fused (D, 3D) projection fan_in = D, fan_out = 3D.
+* "N(0, s)" names the standard deviation s.
+* Key padding is trailing: keys j >= len_b of batch element b are masked,
+  with len_b an integer drawn uniformly from [256, 2048] inclusive.
+* Values are drawn in fp32 and rounded once, round-to-nearest-even, to the
+  workload's dtype; everything downstream sees those rounded values.
+
+Draw order from one CPU ``torch.Generator`` seeded with ``seed``:
+X (or X_q then X_kv), W_QKV, W_O, b_QKV, b_O, then the valid lengths.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention problem: sizes, dtype, masks and the input distributions."""
+
+    name: str
+    dtype: str            # "fp32" or "bf16": the input/weight storage type
+    D: int                # d_model
+    h: int                # number of heads
+    B: int                # batch
+    T_q: int              # query length
+    T_k: int              # key/value length (== T_q for self-attention)
+    cross: bool = False   # keys/values from a second sequence X_kv
+    causal: bool = False
+    padding: Optional[tuple] = None   # (lo, hi) inclusive range of valid key lengths
+    weight_init: str = "xavier"       # "xavier" or ("normal", std)
+    weight_std: float = 0.0
+    bias_std: Optional[float] = None  # None -> zero biases
+
+    @property
+    def d_k(self) -> int:
+        return self.D // self.h
+
+    def flops(self) -> float:
+        """Formula FLOPs: projections 4*T_q*D^2 + 4*T_k*D^2 (8*T*D^2 when
+        T_q == T_k) plus 4*T_q*T_k*D for scores and weighted sum, halved
+        under a causal mask, per batch element (itwiki, 매개변수와 계산량)."""
+        proj = 4.0 * self.T_q * self.D ** 2 + 4.0 * self.T_k * self.D ** 2
+        attn = 4.0 * self.T_q * self.T_k * self.D
+        if self.causal:
+            attn *= 0.5
+        return self.B * (proj + attn)
+
+    def shrink(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads this path is checked and measured on, named by content.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("self_fp32_d512_h8_b2_t128", "fp32", 512, 8, 2, 128, 128,
+                 bias_std=0.02),
+        Workload("causal_bf16_d512_h8_b16_t1024", "bf16", 512, 8, 16, 1024, 1024,
+                 causal=True),
+        Workload("causal_bf16_d1024_h16_b8_t4096", "bf16", 1024, 16, 8, 4096, 4096,
+                 causal=True, bias_std=0.02),
+        Workload("cross_pad_bf16_d512_h8_b32_tq512_tk2048", "bf16", 512, 8, 32, 512,
+                 2048, cross=True, padding=(256, 2048)),
+        Workload("causal_bf16_d4096_h32_b1_t8192", "bf16", 4096, 32, 1, 8192, 8192,
+                 causal=True, weight_init="normal", weight_std=1.0 / 64.0),
+    ]
+}
+
+HEADLINE = "causal_bf16_d1024_h16_b8_t4096"
+
+_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def torch_dtype(w: Workload) -> torch.dtype:
+    return _TORCH_DTYPE[w.dtype]
+
+
+def _uniform(g, shape, a):
+    return torch.rand(shape, generator=g, dtype=torch.float32) * (2.0 * a) - a
+
+
+def _normal(g, shape, std):
+    return torch.randn(shape, generator=g, dtype=torch.float32) * std
+
+
+def make_inputs(w: Workload, seed: int = 0) -> dict:
+    """Draw the inputs of workload ``w`` on the CPU.
+
+    Returns a dict of CPU tensors in the workload dtype (the mask is uint8,
+    nonzero = ignore this key) plus the scalar settings. Zero biases are
+    returned as zero tensors.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    D = w.D
+    x_q = _normal(g, (w.B, w.T_q, D), 1.0)
+    x_kv = _normal(g, (w.B, w.T_k, D), 1.0) if w.cross else None
+    if w.weight_init == "xavier":
+        w_qkv = _uniform(g, (D, 3 * D), math.sqrt(6.0 / (D + 3 * D)))
+        w_o = _uniform(g, (D, D), math.sqrt(6.0 / (D + D)))
+    else:
+        w_qkv = _normal(g, (D, 3 * D), w.weight_std)
+        w_o = _normal(g, (D, D), w.weight_std)
+    if w.bias_std is None:
+        b_qkv = torch.zeros(3 * D)
+        b_o = torch.zeros(D)
+    else:
+        b_qkv = _normal(g, (3 * D,), w.bias_std)
+        b_o = _normal(g, (D,), w.bias_std)
+    mask = None
+    lengths = None
+    if w.padding is not None:
+        lo, hi = w.padding
+        lengths = torch.randint(lo, hi + 1, (w.B,), generator=g)
+        j = torch.arange(w.T_k)
+        mask = (j[None, :] >= lengths[:, None]).to(torch.uint8)
+    dt = torch_dtype(w)
+    out = {
+        "x_q": x_q.to(dt),
+        "x_kv": None if x_kv is None else x_kv.to(dt),
+        "w_qkv": w_qkv.to(dt),
+        "b_qkv": b_qkv.to(dt),
+        "w_o": w_o.to(dt),
+        "b_o": b_o.to(dt),
+        "key_padding_mask": mask,
+        "lengths": lengths,
+        "h": w.h,
+        "causal": w.causal,
+    }
+    return out
+
+
+def as_float64_numpy(t):
+    """Exact upcast of a (bf16 or fp32) CPU tensor to a float64 numpy array."""
+    if t is None:
+        return None
+    return t.to(torch.float64).numpy()

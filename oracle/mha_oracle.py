@@ -1,0 +1,183 @@
+"""Multi-head attention forward, fp64, from the definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+Sources (pages as titled; sections / equations named, no line numbers):
+
+* itwiki "멀티 헤드 어텐션", 수식: Attention(Q,K,V) = softmax(QK^T/sqrt(d_k)) V and
+  MultiHead = Concat(head_1..head_h) W^O, with W_i^Q, W_i^K in R^{d_model x d_k},
+  W_i^V in R^{d_model x d_v}, W^O in R^{h d_v x d_model}.
+* itwiki, 텐서 모양으로 본 계산: the three D x D projections are usually one
+  D x 3D matrix; a "head" is a slice of that output, split by view+transpose
+  to (B, h, T, d_k); scores (B, h, T, T); softmax over the last axis; weighted
+  sum (B, h, T, d_k); concat by transpose+reshape to (B, T, D); output
+  projection W^O.
+* iamjaehka13.blog "[Deep Learning 5] Attention의 내부 계산", §9: causal mask
+  M_ij = 0 for j <= i and -inf for j > i, added to the scaled scores, so a
+  future key's weight is exactly exp(-inf) = 0; §10: row-wise softmax, rows
+  non-negative and summing to 1; §13: O = A V; §18: concat then one
+  d_model x d_model W_O; §19: cross-attention takes Q from the target
+  sequence and K, V from the source sequence.
+* molayo1419.me "MHA란 무엇인가?", trap 2: key_padding_mask True = ignore
+  this key; trap 3: a row whose keys are all ignored becomes 0/0 = NaN.
+
+Conventions (readings where the pages leave a step open):
+
+* Weights are stored as y = x . W: W_QKV is (D, 3D) with column blocks
+  [Q | K | V]; inside each block head i owns columns [i*d_k, (i+1)*d_k).
+* Cross-attention with one fused W_QKV: Q = X_q W_QKV[:, :D] + b[:D] and
+  [K | V] = X_kv W_QKV[:, D:] + b[D:].
+* The scale is 1/sqrt(d_k) (one page prints QK^T/d_k; every other statement,
+  including the variance argument of §8 on iamjaehka13.blog, has the root).
+* softmax subtracts the row maximum before exponentiating. In exact
+  arithmetic this changes nothing (the factor exp(-max) cancels); it only
+  keeps exp() in range. A row with every key masked is 0/0 = NaN.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def linear(x: np.ndarray, w: np.ndarray, b) -> np.ndarray:
+    """y = x . W + b for x (..., D_in), W (D_in, D_out), b (D_out,) or None."""
+    y = x @ w
+    if b is not None:
+        y = y + b
+    return y
+
+
+def split_heads(y: np.ndarray, h: int) -> np.ndarray:
+    """(B, T, D) -> (B, h, T, d_k): head i is columns [i*d_k, (i+1)*d_k)."""
+    B, T, D = y.shape
+    if D % h != 0:
+        raise ValueError("embed_dim must be divisible by num_heads")
+    return y.reshape(B, T, h, D // h).transpose(0, 2, 1, 3)
+
+
+def concat_heads(o: np.ndarray) -> np.ndarray:
+    """(B, h, T, d_v) -> (B, T, h*d_v): head i lands in columns [i*d_v, (i+1)*d_v)."""
+    B, h, T, d = o.shape
+    return o.transpose(0, 2, 1, 3).reshape(B, T, h * d)
+
+
+def masked_scores(q: np.ndarray, k: np.ndarray, causal: bool, key_padding_mask,
+                  q_pos=None) -> np.ndarray:
+    """QK^T / sqrt(d_k) + M for q (B, h, Tq, d_k), k (B, h, Tk, d_k).
+
+    ``causal`` puts -inf at key j > query position i. ``key_padding_mask``
+    (B, Tk), nonzero = ignore, puts -inf at those keys. ``q_pos`` gives the
+    sequence positions of the query rows (default 0..Tq-1), so that a subset
+    of rows can be evaluated on its own.
+    """
+    d_k = q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(d_k)
+    Tq, Tk = s.shape[-2], s.shape[-1]
+    if causal:
+        i = np.arange(Tq) if q_pos is None else np.asarray(q_pos)
+        future = np.arange(Tk)[None, :] > i[:, None]          # (Tq, Tk)
+        s = np.where(future[None, None], -np.inf, s)
+    if key_padding_mask is not None:
+        ignore = np.asarray(key_padding_mask) != 0              # (B, Tk)
+        s = np.where(ignore[:, None, None, :], -np.inf, s)
+    return s
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis; an all -inf row gives 0/0 = NaN."""
+    m = np.max(s, axis=-1, keepdims=True)
+    m = np.where(np.isneginf(m), 0.0, m)   # all-masked row: exp(-inf - 0) = 0
+    e = np.exp(s - m)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention(q, k, v, causal=False, key_padding_mask=None, q_pos=None):
+    """softmax(QK^T/sqrt(d_k) + M) V per (batch, head). Returns (O, A)."""
+    a = softmax_rows(masked_scores(q, k, causal, key_padding_mask, q_pos))
+    return a @ v, a
+
+
+def _as64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def _qkv(x_q, x_kv, w_qkv, b_qkv, D):
+    """Fused projection: one D x 3D matrix for self-attention; for
+    cross-attention Q comes from x_q and K, V from x_kv."""
+    if x_kv is None:
+        y = linear(x_q, w_qkv, b_qkv)
+        return y[..., :D], y[..., D:2 * D], y[..., 2 * D:]
+    bq = None if b_qkv is None else b_qkv[:D]
+    bkv = None if b_qkv is None else b_qkv[D:]
+    q = linear(x_q, w_qkv[:, :D], bq)
+    kv = linear(x_kv, w_qkv[:, D:], bkv)
+    return q, kv[..., :D], kv[..., D:]
+
+
+def mha_forward(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
+                key_padding_mask=None, return_intermediates=False):
+    """Y = Concat(head_1..head_h) W^O + b_O for batch-first inputs.
+
+    x_q (B, T_q, D); x_kv (B, T_k, D) or None for self-attention;
+    w_qkv (D, 3D); b_qkv (3D,) or None; w_o (D, D); b_o (D,) or None;
+    key_padding_mask (B, T_k), nonzero = ignore, or None.
+    Everything is evaluated in float64.
+    """
+    x_q, x_kv, w_qkv, b_qkv, w_o, b_o = map(_as64, (x_q, x_kv, w_qkv, b_qkv, w_o, b_o))
+    B, T_q, D = x_q.shape
+    if D % h != 0:
+        raise ValueError("embed_dim must be divisible by num_heads")
+    if causal and x_kv is not None and x_kv.shape[1] != T_q:
+        raise ValueError("causal mask needs T_q == T_k")
+    q, k, v = _qkv(x_q, x_kv, w_qkv, b_qkv, D)
+    qh, kh, vh = (split_heads(t, h) for t in (q, k, v))
+    o, a = attention(qh, kh, vh, causal, key_padding_mask)
+    o_cat = concat_heads(o)
+    y = linear(o_cat, w_o, b_o)
+    if return_intermediates:
+        return y, {"q": qh, "k": kh, "v": vh, "a": a, "o": o_cat}
+    return y
+
+
+def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
+                     causal=False, key_padding_mask=None):
+    """Y[b, t, :] for selected query rows only.
+
+    ``rows`` maps a batch index b to a 1-D array of query positions t. The
+    keys and values of batch b are projected in full; only the selected query
+    rows are projected, attended and output-projected. Each row's result is
+    the same as that row of ``mha_forward`` (rows are independent).
+    Returns {b: (len(rows[b]), D) float64 array}.
+    """
+    w_qkv, b_qkv, w_o, b_o = map(_as64, (w_qkv, b_qkv, w_o, b_o))
+    D = w_qkv.shape[0]
+    out = {}
+    for b, ts in rows.items():
+        ts = np.asarray(ts, dtype=np.int64)
+        xq_b = _as64(x_q[b])[ts][None]                       # (1, n, D)
+        xkv_b = _as64((x_q if x_kv is None else x_kv)[b])[None]
+        bq = None if b_qkv is None else b_qkv[:D]
+        bkv = None if b_qkv is None else b_qkv[D:]
+        q = linear(xq_b, w_qkv[:, :D], bq)
+        kv = linear(xkv_b, w_qkv[:, D:], bkv)
+        k, v = kv[..., :D], kv[..., D:]
+        mask_b = None if key_padding_mask is None else np.asarray(key_padding_mask)[b:b + 1]
+        qh, kh, vh = (split_heads(t, h) for t in (q, k, v))
+        o, _ = attention(qh, kh, vh, causal, mask_b, q_pos=ts)
+        out[b] = linear(concat_heads(o), w_o, b_o)[0]
+    return out
+
+
+def param_count(D: int, h: int, bias: bool = True) -> int:
+    """Number of parameters of one MHA layer as this module stores them:
+    W_QKV (D x 3D), W_O (D x D) and, with ``bias``, b_QKV (3D) and b_O (D).
+    The head count only slices the same matrices (molayo1419.me, parameter
+    table: 4E^2 + 4E for every num_heads)."""
+    if D % h != 0:
+        raise ValueError("embed_dim must be divisible by num_heads")
+    shapes = [(D, 3 * D), (D, D)] + ([(3 * D,), (D,)] if bias else [])
+    return int(sum(np.prod(s) for s in shapes))
