@@ -1,0 +1,199 @@
+"""Throughput of the multi-head attention forward pass on one MI355X.
+
+One step = one mha_forward call over one batch of seeded synthetic input
+(weight preparation, QKV projection, fused attention, output projection and
+the fp32 early-row pass), inputs resident in HBM. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline]
+
+Beside the headline rate the line carries:
+  roofline      the dominant kernel's algorithmic FLOPs per launch divided by
+                its average launch time (HIP events on the launch stream,
+                around each of the timed calls), against the MI355X dense
+                fp16/bf16 MFMA peak; `traffic` is the HBM bytes per launch from
+                the committed rocprofv3 counter summary, or null when that
+                summary was taken on a different kernel source.
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample of
+                the same workload (one batch element).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MHA fwd TFLOP/s + % bf16 MFMA peak, D=1024 h=16 T=4096 causal, 1 GPU"
+PEAK_MFMA_16BIT_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.txt")
+KERNEL_SOURCES = {
+    "attention": ["transformer_head_attention_amd/csrc/attn16.hip",
+                  "transformer_head_attention_amd/csrc/device_common.h"],
+}
+
+
+def source_digest(stage: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stage_flops(w, stage: str) -> float:
+    """Algorithmic FLOPs of one launch of a stage (formula counts)."""
+    D = w.D
+    if stage == "attention":
+        f = 4.0 * w.T_q * w.T_k * D * w.B
+        return f * 0.5 if w.causal else f
+    if stage == "qkv_proj":
+        return 2.0 * w.B * (w.T_q * D * D + w.T_k * D * 2 * D)
+    if stage == "out_proj":
+        return 2.0 * w.B * w.T_q * D * D
+    return 0.0
+
+
+def read_traffic(stage: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest(stage):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp):
+    """fp64 oracle on batch element 0 of the workload, timed on this host."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from mha_inputs import as_float64_numpy as f
+    from oracle import mha_oracle
+
+    mask = inp["key_padding_mask"]
+    t0 = time.perf_counter()
+    mha_oracle.mha_forward(
+        f(inp["x_q"][:1]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]), f(inp["b_o"]), w.h,
+        x_kv=None if inp["x_kv"] is None else f(inp["x_kv"][:1]), causal=w.causal,
+        key_padding_mask=None if mask is None else mask[:1].numpy())
+    dt = time.perf_counter() - t0
+    flops = w.flops() / w.B
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    del np
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"batch element 0 of {w.B} (all {w.T_q} query rows, all heads), "
+                      f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 numpy"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        return 2
+
+    import torch
+    import transformer_head_attention_amd as mha
+    from mha_inputs import WORKLOADS, HEADLINE, make_inputs
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    inp = make_inputs(w, seed=0)
+    dev = torch.device("cuda:0")
+    t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    m = mha.MultiHeadAttention(w.D, w.h, w.dtype)
+    ws = m.workspace(w.B, w.T_q, w.T_k, dev)
+    y = torch.empty(w.B, w.T_q, w.D, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        m.forward(t["x_q"], t["w_qkv"], t["w_o"], b_qkv=t["b_qkv"], b_o=t["b_o"], x_kv=t["x_kv"],
+                  causal=w.causal, key_padding_mask=t["key_padding_mask"], out=y, workspace=ws,
+                  stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    mha._check(mha.mha_profile_begin(m.handle, args.steps), "mha_profile_begin")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    st, stages, ncalls = mha.mha_profile_end(m.handle)
+    mha._check(st, "mha_profile_end")
+
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    dom = max(("qkv_proj", "attention", "out_proj"), key=lambda s: stages[s])
+    dom_ms = stages[dom]
+    achieved = stage_flops(w, dom) / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
+    traffic = read_traffic(dom) if dom in KERNEL_SOURCES else None
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "T_q": w.T_q, "T_k": w.T_k, "D": w.D, "h": w.h,
+                   "d_k": w.d_k, "causal": w.causal, "cross": w.cross,
+                   "key_padding": w.padding is not None, "gflop_per_step": round(flops / 1e9, 3),
+                   "intermediates": "fp16 Q/K/V/P/O, fp32 accumulate, fp32 Y"},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_MFMA_16BIT_TFLOPS, 2),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": None if achieved is None else round(achieved, 2),
+            "peak": PEAK_MFMA_16BIT_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": None if achieved is None else round(achieved / PEAK_MFMA_16BIT_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,136 @@
+/*
+ * mha.h -- C ABI of the MI355X (gfx950) multi-head attention forward pass.
+ *
+ * What is computed (fused projection, head split, scaled scores with an
+ * optional causal or key-padding mask, row softmax, weighted sum, head concat,
+ * output projection):
+ *
+ *   itwiki "멀티 헤드 어텐션", section 수식:
+ *     Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V,
+ *     MultiHead = Concat(head_1, ..., head_h) W^O, d_k = d_v = d_model / h.
+ *   same page, section 텐서 모양으로 본 계산: the three D x D projections are
+ *     one D x 3D matrix; a head is a column slice of its output.
+ *   iamjaehka13.blog "[Deep Learning 5] Attention의 내부 계산", §9 (causal mask:
+ *     key j > query i gets -inf, so its weight is exactly 0), §10 (row
+ *     softmax), §13 (O = A V), §18 (concat, one d_model x d_model W_O),
+ *     §19 (cross-attention: Q from the target, K and V from the source).
+ *   molayo1419.me "MHA란 무엇인가?", trap 2 (key_padding_mask: nonzero/True
+ *     means IGNORE the key) and trap 3 (every key ignored -> 0/0 -> NaN).
+ *
+ * Conventions:
+ *   - Batch-first only: every activation is (B, T, D) row-major.
+ *   - Weights multiply from the right, y = x . W + b. W_QKV is (D, 3D)
+ *     row-major with column blocks [Q | K | V]; head i owns columns
+ *     [i*d_k, (i+1)*d_k) inside each block. W_O is (D, D) row-major.
+ *     (torch.nn.Linear / nn.MultiheadAttention store the transpose.)
+ *   - Cross-attention (x_kv != NULL): Q = x_q W_QKV[:, 0:D] + b_QKV[0:D],
+ *     [K | V] = x_kv W_QKV[:, D:3D] + b_QKV[D:3D].
+ *   - KEY PADDING MASK: NONZERO = THIS KEY IS IGNORED (nn.MultiheadAttention's
+ *     key_padding_mask convention, NOT the SDPA boolean attn_mask convention).
+ *   - causal = 1 masks keys j > i (requires T_q == T_k). It is a real mask,
+ *     not a hint that some other mask is causal.
+ *   - A query row whose keys are all masked yields NaN in that row of the
+ *     attention output, hence in that row of y.
+ *   - dtype MHA_F32: every input, weight and bias is fp32 and the path
+ *     computes in fp32. dtype MHA_BF16: inputs, weights and biases are bf16;
+ *     products accumulate in fp32 and y is always fp32.
+ *
+ * Memory and execution:
+ *   - Every data pointer is a DEVICE pointer on the current HIP device and
+ *     must be 16-byte aligned. The caller owns all buffers, including the
+ *     workspace; the library allocates no device memory.
+ *   - mha_forward enqueues its kernels on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns without waiting. Argument errors are
+ *     returned before anything is enqueued; launch failures return
+ *     MHA_ERR_HIP; faults during execution surface at the next
+ *     synchronisation, as with any HIP call.
+ *   - A handle is immutable after mha_create, except for the profiling state
+ *     below. Calls on one handle may run concurrently only if their
+ *     workspaces differ and no profiling is active.
+ *
+ * Supported on the GPU: d_k = D / h in {64, 128}, D a multiple of 128,
+ * B, T_q, T_k >= 1. fp16 overflow bound: every projected Q, K, V value and
+ * every attention output must stay below 65504 in magnitude (bf16 path).
+ */
+#ifndef MHA_H
+#define MHA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mha_handle* mha_handle_t;
+
+typedef enum { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype_t;
+
+typedef enum {
+  MHA_OK = 0,
+  MHA_ERR_INVALID_ARG = 1, /* bad sizes, NULL/misaligned pointers, D % h != 0, causal with T_q != T_k */
+  MHA_ERR_UNSUPPORTED = 2, /* valid MHA, but outside what the kernels handle (d_k, D % 128) */
+  MHA_ERR_WORKSPACE = 3,   /* workspace smaller than mha_workspace_size() */
+  MHA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} mha_status_t;
+
+/* Create a handle for d_model = D, h heads and the given dtype (host only,
+ * no device work). D % h != 0 -> MHA_ERR_INVALID_ARG (embed_dim must be
+ * divisible by num_heads); d_k not in {64, 128} or D % 128 != 0 ->
+ * MHA_ERR_UNSUPPORTED. On error *out is set to NULL. */
+mha_status_t mha_create(mha_handle_t* out, int d_model, int num_heads, mha_dtype_t dtype);
+
+/* Bytes of device workspace mha_forward needs for these sizes (0 if the
+ * handle or sizes are invalid). Pass T_k = T_q for self-attention. */
+size_t mha_workspace_size(mha_handle_t handle, int B, int T_q, int T_k);
+
+/* One forward pass: y = MultiHead(x_q, x_kv) as described above.
+ *   x_q   (B, T_q, D)  dtype   queries (and keys/values if x_kv == NULL)
+ *   x_kv  (B, T_k, D)  dtype   keys/values source, or NULL for self-attention
+ *                              (then T_k must equal T_q)
+ *   w_qkv (D, 3D)      dtype   row-major, y = x . W
+ *   b_qkv (3D)         dtype   or NULL (zero bias)
+ *   w_o   (D, D)       dtype   row-major
+ *   b_o   (D)          dtype   or NULL (zero bias)
+ *   causal             0 or 1
+ *   key_padding_mask   (B, T_k) uint8, NONZERO = IGNORE, or NULL
+ *   y     (B, T_q, D)  fp32    output, fully overwritten
+ *   workspace          device scratch of >= workspace_bytes bytes, contents
+ *                      undefined on entry and exit; must not overlap any
+ *                      other argument
+ *   stream             hipStream_t or NULL
+ */
+mha_status_t mha_forward(mha_handle_t handle,
+                         const void* x_q, const void* x_kv,
+                         const void* w_qkv, const void* b_qkv,
+                         const void* w_o, const void* b_o,
+                         int B, int T_q, int T_k, int causal,
+                         const unsigned char* key_padding_mask,
+                         float* y,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Release a handle (NULL is accepted). */
+mha_status_t mha_destroy(mha_handle_t handle);
+
+/* Static, human-readable name of a status code. */
+const char* mha_status_string(mha_status_t status);
+
+/* ---- Per-stage timing (measurement only; no effect on results) ----------
+ * mha_profile_begin: subsequent mha_forward calls on this handle record HIP
+ * events around each stage, for at most max_calls calls.
+ * mha_profile_end: waits for the recorded events, writes the AVERAGE duration
+ * in milliseconds of each stage over the recorded calls into
+ * stage_ms[0 .. MHA_NUM_STAGES-1] (host array), the number of recorded calls
+ * into *n_calls, and stops recording. Stages that did not run read 0. */
+#define MHA_NUM_STAGES 5
+mha_status_t mha_profile_begin(mha_handle_t handle, int max_calls);
+mha_status_t mha_profile_end(mha_handle_t handle, float* stage_ms, int* n_calls);
+/* Static name of stage s ("prep", "qkv_proj", "attention", "out_proj",
+ * "early_rows"), or NULL. */
+const char* mha_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H */

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI vs the fp64 oracle.
+
+Error metric (the workloads' tolerance contract): max |Y_gpu - Y_ref| divided
+by the RMS of Y_ref, <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs.
+NaN positions (rows whose keys are all masked) must match exactly.
+
+* Mid-size cases compare every output element; their sizes span several
+  tiles and end in ragged tails.
+* The five full-size workloads run exactly as the benchmark launches them;
+  the oracle evaluates sampled rows (all early causal rows of two batch
+  elements, the last rows, and uniformly drawn rows whose RMS normalises the
+  error).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mha_inputs import WORKLOADS, make_inputs, as_float64_numpy
+from oracle import mha_oracle as mo
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import transformer_head_attention_amd as m
+    return m
+
+
+def _dev(t):
+    return None if t is None else t.to("cuda:0")
+
+
+def run_gpu(lib, w, inp, stream=None, none_bias=False, mod=None):
+    m = mod or lib.MultiHeadAttention(w.D, w.h, w.dtype)
+    y = m.forward(_dev(inp["x_q"]), _dev(inp["w_qkv"]), _dev(inp["w_o"]),
+                  b_qkv=None if none_bias else _dev(inp["b_qkv"]),
+                  b_o=None if none_bias else _dev(inp["b_o"]),
+                  x_kv=_dev(inp["x_kv"]), causal=inp["causal"],
+                  key_padding_mask=_dev(inp["key_padding_mask"]), stream=stream)
+    torch.cuda.synchronize()
+    return y.cpu().double().numpy()
+
+
+def _np_mask(inp):
+    m = inp["key_padding_mask"]
+    return None if m is None else m.numpy()
+
+
+def oracle_full(inp):
+    f = as_float64_numpy
+    return mo.mha_forward(f(inp["x_q"]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]),
+                          f(inp["b_o"]), inp["h"], x_kv=f(inp["x_kv"]), causal=inp["causal"],
+                          key_padding_mask=_np_mask(inp))
+
+
+def oracle_rows(inp, rows):
+    f = as_float64_numpy
+    return mo.mha_forward_rows(f(inp["x_q"]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]),
+                               f(inp["b_o"]), inp["h"], rows, x_kv=f(inp["x_kv"]),
+                               causal=inp["causal"], key_padding_mask=_np_mask(inp))
+
+
+def rel_err(y, ref, rms=None):
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan_ref), "NaN positions differ"
+    ok = ~nan_ref
+    if rms is None:
+        rms = math.sqrt(float(np.mean(ref[ok] ** 2)))
+    return float(np.max(np.abs(y[ok] - ref[ok]))) / rms
+
+
+# ---------------------------------------------------------------- mid-size
+
+W = WORKLOADS
+MID = [
+    ("fp32 self, the full d512/h8/b2/t128 workload", W["self_fp32_d512_h8_b2_t128"], {}),
+    ("fp32 causal ragged", W["self_fp32_d512_h8_b2_t128"], dict(T_q=201, T_k=201, causal=True)),
+    ("fp32 cross padded", W["self_fp32_d512_h8_b2_t128"],
+     dict(B=3, T_q=77, T_k=150, cross=True, padding=(1, 150))),
+    ("fp32 d_k=128", W["self_fp32_d512_h8_b2_t128"], dict(D=1024, h=8, T_q=99, T_k=99,
+                                                          causal=True)),
+    ("bf16 causal d512 ragged", W["causal_bf16_d512_h8_b16_t1024"], dict(B=2, T_q=300, T_k=300)),
+    ("bf16 causal d1024 ragged", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=1, T_q=777,
+                                                                            T_k=777)),
+    ("bf16 non-causal self", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=2, T_q=257, T_k=257,
+                                                                        causal=False)),
+    ("bf16 cross padded ragged", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
+     dict(B=3, T_q=200, T_k=333, padding=(40, 333))),
+    ("bf16 causal d_k=128", W["causal_bf16_d4096_h32_b1_t8192"], dict(T_q=300, T_k=300)),
+    ("bf16 causal + padding", W["causal_bf16_d512_h8_b16_t1024"],
+     dict(B=3, T_q=190, T_k=190, padding=(150, 190))),
+    ("bf16 T=1 causal", W["causal_bf16_d512_h8_b16_t1024"], dict(B=3, T_q=1, T_k=1)),
+    ("bf16 T=1 self", W["causal_bf16_d512_h8_b16_t1024"], dict(B=3, T_q=1, T_k=1, causal=False)),
+    ("bf16 T_q=1 cross", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
+     dict(B=2, T_q=1, T_k=5, padding=(1, 5))),
+    ("bf16 T=65 causal", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=2, T_q=65, T_k=65)),
+    ("bf16 T=129 causal d_k=128", W["causal_bf16_d4096_h32_b1_t8192"], dict(D=1024, h=8,
+                                                                              T_q=129, T_k=129)),
+]
+
+
+@pytest.mark.parametrize("name,base,kw", MID, ids=[m[0] for m in MID])
+def test_mid_size_parity(lib, name, base, kw):
+    w = base.shrink(name=name, **kw)
+    _say(f"[parity] {name}: {w}")
+    inp = make_inputs(w, seed=3)
+    y = run_gpu(lib, w, inp)
+    ref = oracle_full(inp)
+    err = rel_err(y, ref)
+    _say(f"[parity] {name}: err/rms = {err:.3e} (tol {TOL[w.dtype]})")
+    assert err <= TOL[w.dtype]
+
+
+def test_all_masked_rows_are_nan(lib):
+    w = W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"].shrink(B=3, T_q=70, T_k=90, padding=None)
+    _say(f"[parity] all-masked batch element: {w}")
+    inp = make_inputs(w, seed=4)
+    mask = torch.zeros(3, 90, dtype=torch.uint8)
+    mask[1, :] = 1          # every key of batch element 1 ignored
+    mask[2, 50:] = 1
+    inp["key_padding_mask"] = mask
+    y = run_gpu(lib, w, inp)
+    assert np.isnan(y[1]).all()
+    assert np.isfinite(y[0]).all() and np.isfinite(y[2]).all()
+    assert rel_err(y, oracle_full(inp)) <= TOL["bf16"]
+
+
+def test_interior_mask_holes(lib):
+    """A general (non-trailing) padding mask, masking whole 64-key tiles too."""
+    w = W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"].shrink(B=2, T_q=100, T_k=300, padding=None)
+    _say(f"[parity] interior mask holes: {w}")
+    inp = make_inputs(w, seed=5)
+    mask = torch.zeros(2, 300, dtype=torch.uint8)
+    mask[0, 0:64] = 1
+    mask[0, 100:190] = 1
+    mask[1, ::3] = 1
+    inp["key_padding_mask"] = mask
+    assert rel_err(run_gpu(lib, w, inp), oracle_full(inp)) <= TOL["bf16"]
+
+
+def test_deterministic_and_null_bias_equals_zero_bias(lib):
+    w = W["causal_bf16_d512_h8_b16_t1024"].shrink(B=2, T_q=333, T_k=333)
+    _say(f"[parity] determinism / null bias: {w}")
+    inp = make_inputs(w, seed=6)       # zero biases
+    y1 = run_gpu(lib, w, inp)
+    y2 = run_gpu(lib, w, inp)
+    y3 = run_gpu(lib, w, inp, none_bias=True)
+    assert np.array_equal(y1, y2)
+    assert np.array_equal(y1, y3)
+
+
+def test_side_stream_and_workspace_reuse(lib):
+    w = W["causal_bf16_d1024_h16_b8_t4096"].shrink(B=1, T_q=400, T_k=400)
+    _say(f"[parity] side stream + reused workspace: {w}")
+    m = lib.MultiHeadAttention(w.D, w.h, "bf16")
+    inp = make_inputs(w, seed=7)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y_big = run_gpu(lib, w, inp, stream=s.cuda_stream, mod=m)
+    w2 = w.shrink(T_q=130, T_k=130)
+    inp2 = make_inputs(w2, seed=8)
+    y_small = run_gpu(lib, w2, inp2, mod=m)     # smaller call into the larger workspace
+    assert rel_err(y_big, oracle_full(inp)) <= TOL["bf16"]
+    assert rel_err(y_small, oracle_full(inp2)) <= TOL["bf16"]
+
+
+# -------------------------------------------------------------- full sizes
+
+def _sample_rows(w, rng):
+    """{b: positions}: uniform rows for the RMS, plus early and last rows."""
+    bs = sorted({0, w.B - 1})
+    uni = {b: set(rng.choice(w.T_q, size=min(w.T_q, 48), replace=False).tolist()) for b in bs}
+    extra = {b: set(range(min(w.T_q, 72))) | {w.T_q - 1, w.T_q - 2} for b in bs}
+    return bs, uni, extra
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_workload(lib, name):
+    w = WORKLOADS[name]
+    _say(f"[parity] full size {name}")
+    inp = make_inputs(w, seed=0)
+    y = run_gpu(lib, w, inp)
+    if w.B * w.T_q <= 4096 and w.T_k <= 1024:
+        err = rel_err(y, oracle_full(inp))
+    else:
+        rng = np.random.default_rng(1234)
+        bs, uni, extra = _sample_rows(w, rng)
+        rows = {b: np.array(sorted(uni[b] | extra[b])) for b in bs}
+        ref_rows = oracle_rows(inp, rows)
+        uni_ref = np.concatenate([ref_rows[b][np.isin(rows[b], sorted(uni[b]))] for b in bs])
+        rms = math.sqrt(float(np.mean(uni_ref[~np.isnan(uni_ref)] ** 2)))
+        err = max(rel_err(y[b, rows[b]], ref_rows[b], rms) for b in bs)
+    _say(f"[parity] full size {name}: err/rms = {err:.3e} (tol {TOL[w.dtype]})")
+    assert np.isfinite(y).all()
+    assert err <= TOL[w.dtype]

@@ -1,0 +1,184 @@
+"""MI355X (gfx950) multi-head attention forward pass: Python binding.
+
+A thin ctypes layer over ``libmha.so``, whose C ABI is declared in
+``include/mha.h``. The functions below carry the C names and only marshal
+arguments; every step of the computation runs in the library's HIP kernels.
+torch is used for device memory and streams only.
+
+There is no fallback: if ``libmha.so`` has not been built, importing this
+package raises ImportError.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmha.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(hipcc, gfx950). The multi-head attention path has no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MHA_F32, MHA_BF16 = 0, 1
+MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP = range(5)
+MHA_NUM_STAGES = 5
+
+EXPORTED = ("mha_create", "mha_workspace_size", "mha_forward", "mha_destroy",
+            "mha_status_string", "mha_profile_begin", "mha_profile_end", "mha_stage_name")
+
+_vp, _int, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_lib.mha_create.argtypes = [ctypes.POINTER(_vp), _int, _int, _int]
+_lib.mha_create.restype = _int
+_lib.mha_workspace_size.argtypes = [_vp, _int, _int, _int]
+_lib.mha_workspace_size.restype = _sz
+_lib.mha_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
+                             _vp, _vp, _sz, _vp]
+_lib.mha_forward.restype = _int
+_lib.mha_destroy.argtypes = [_vp]
+_lib.mha_destroy.restype = _int
+_lib.mha_status_string.argtypes = [_int]
+_lib.mha_status_string.restype = ctypes.c_char_p
+_lib.mha_profile_begin.argtypes = [_vp, _int]
+_lib.mha_profile_begin.restype = _int
+_lib.mha_profile_end.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_int)]
+_lib.mha_profile_end.restype = _int
+_lib.mha_stage_name.argtypes = [_int]
+_lib.mha_stage_name.restype = ctypes.c_char_p
+
+
+class MHAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {mha_status_string(status)}")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != MHA_OK:
+        raise MHAError(status, where)
+
+
+# ---- C names ---------------------------------------------------------------
+
+def mha_status_string(status: int) -> str:
+    return _lib.mha_status_string(int(status)).decode()
+
+
+def mha_stage_name(stage: int):
+    s = _lib.mha_stage_name(int(stage))
+    return None if s is None else s.decode()
+
+
+def mha_create(d_model: int, num_heads: int, dtype: int):
+    """Returns (status, handle); handle is None on error."""
+    h = _vp()
+    st = _lib.mha_create(ctypes.byref(h), int(d_model), int(num_heads), int(dtype))
+    return st, (h.value if st == MHA_OK else None)
+
+
+def mha_workspace_size(handle, B: int, T_q: int, T_k: int) -> int:
+    return int(_lib.mha_workspace_size(handle, int(B), int(T_q), int(T_k)))
+
+
+def mha_forward(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k, causal,
+                key_padding_mask, y, workspace, workspace_bytes, stream) -> int:
+    """Raw call: every pointer argument is an int device address (or 0/None)."""
+    return _lib.mha_forward(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, int(B), int(T_q),
+                            int(T_k), int(causal), key_padding_mask, y, workspace,
+                            int(workspace_bytes), stream)
+
+
+def mha_destroy(handle) -> int:
+    return _lib.mha_destroy(handle)
+
+
+def mha_profile_begin(handle, max_calls: int) -> int:
+    return _lib.mha_profile_begin(handle, int(max_calls))
+
+
+def mha_profile_end(handle):
+    """Returns (status, {stage name: average ms}, n_calls)."""
+    arr = (ctypes.c_float * MHA_NUM_STAGES)()
+    n = _int(0)
+    st = _lib.mha_profile_end(handle, arr, ctypes.byref(n))
+    return st, {mha_stage_name(i): float(arr[i]) for i in range(MHA_NUM_STAGES)}, n.value
+
+
+# ---- torch-tensor convenience wrapper (marshalling only) ---------------------
+
+class MultiHeadAttention:
+    """Holds an ``mha_handle_t`` for (d_model, num_heads, dtype) and calls
+    ``mha_forward`` on torch CUDA tensors.
+
+    dtype is "bf16" (bf16 inputs/weights, fp32 output) or "fp32".
+    """
+
+    def __init__(self, d_model: int, num_heads: int, dtype: str = "bf16"):
+        import torch
+        self._torch = torch
+        self.d_model, self.num_heads = d_model, num_heads
+        self.dtype = dtype
+        self._tdtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+        st, h = mha_create(d_model, num_heads, MHA_BF16 if dtype == "bf16" else MHA_F32)
+        _check(st, "mha_create")
+        self.handle = h
+        self._ws = None
+
+    def close(self):
+        if self.handle is not None:
+            mha_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, B: int, T_q: int, T_k: int) -> int:
+        return mha_workspace_size(self.handle, B, T_q, T_k)
+
+    def workspace(self, B: int, T_q: int, T_k: int, device):
+        n = self.workspace_size(B, T_q, T_k)
+        if n == 0:
+            raise MHAError(MHA_ERR_INVALID_ARG, "mha_workspace_size")
+        if self._ws is None or self._ws.numel() < n or self._ws.device != device:
+            self._ws = self._torch.empty(n, dtype=self._torch.uint8, device=device)
+        return self._ws
+
+    def _ptr(self, t, dtype=None):
+        if t is None:
+            return None
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous CUDA tensors")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"expected {dtype}, got {t.dtype}")
+        return t.data_ptr()
+
+    def forward(self, x_q, w_qkv, w_o, b_qkv=None, b_o=None, x_kv=None, causal=False,
+                key_padding_mask=None, out=None, workspace=None, stream=None):
+        torch = self._torch
+        B, T_q, D = x_q.shape
+        T_k = T_q if x_kv is None else x_kv.shape[1]
+        if out is None:
+            out = torch.empty(B, T_q, D, dtype=torch.float32, device=x_q.device)
+        if workspace is None:
+            workspace = self.workspace(B, T_q, T_k, x_q.device)
+        if key_padding_mask is not None and key_padding_mask.dtype != torch.uint8:
+            key_padding_mask = key_padding_mask.to(torch.uint8)
+        if stream is None:
+            stream = torch.cuda.current_stream(x_q.device).cuda_stream
+        dt = self._tdtype
+        st = mha_forward(self.handle, self._ptr(x_q, dt), self._ptr(x_kv, dt),
+                         self._ptr(w_qkv, dt), self._ptr(b_qkv, dt), self._ptr(w_o, dt),
+                         self._ptr(b_o, dt), B, T_q, T_k, 1 if causal else 0,
+                         self._ptr(key_padding_mask), self._ptr(out, torch.float32),
+                         workspace.data_ptr(), workspace.numel(), stream)
+        _check(st, "mha_forward")
+        return out
+
+    __call__ = forward

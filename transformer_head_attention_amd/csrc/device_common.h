@@ -1,0 +1,79 @@
+// Device-side building blocks shared by the gfx950 kernels: 16-bit element
+// types, MFMA wrappers and small vector helpers.
+//
+// MFMA operand/result lane layouts relied on (wave64, gfx950):
+//   v_mfma_f32_32x32x16_{f16,bf16}: lane l supplies row (A) / column (B)
+//     l % 32 and 8 k-values selected by l / 32; A and B use the same k map.
+//     Result: lane l holds column j = l % 32, and for r = 0..15 the row
+//     i = 8*(r/4) + 4*(l/32) + (r%4).
+//   v_mfma_f32_16x16x4_f32: lane l supplies row (A) / column (B) l % 16 at
+//     k = l / 16. Result: lane l holds column l % 16, rows 4*(l/16) + r.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+// Plain clang vectors for raw 16/8-byte moves (HIP's uint4 is a struct that
+// keeps register arrays of it from being promoted out of scratch).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Tag types for the two 16-bit MFMA input formats.
+struct BF16 {};
+struct F16 {};
+
+template <typename Tag>
+__device__ __forceinline__ f32x16_t mfma32x32x16(const u32x4& a, const u32x4& b, f32x16_t c);
+
+template <>
+__device__ __forceinline__ f32x16_t mfma32x32x16<BF16>(const u32x4& a, const u32x4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16_t mfma32x32x16<F16>(const u32x4& a, const u32x4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x4f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> fp16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t float_to_f16_bits(float x) {
+  _Float16 h = static_cast<_Float16>(x);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Two fp32 -> packed fp16x2 (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  half2_t h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint16_t v) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, v));
+}
+
+// Load one element of a bias vector stored as bf16 or fp32 bits.
+__device__ __forceinline__ float load_bias_bf16(const uint16_t* b, int i) {
+  return b ? bf16_bits_to_float(b[i]) : 0.0f;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace mha

@@ -1,0 +1,74 @@
+// Internal launch interface between the C ABI (mha_api.cpp) and the kernels.
+// Not part of the public ABI; every pointer here is a device pointer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mha {
+
+// Rows of each causal sequence that the bf16 path evaluates a second time in
+// fp32 (query rows t < kEarlyRows attend only to keys t' <= t < kEarlyRows).
+constexpr int kEarlyRows = 64;
+
+// ---- preparation ---------------------------------------------------------
+// WT[n][k] = W[k][n] for a (K x N) bf16 matrix; converted to fp16 if to_f16.
+hipError_t launch_transpose_bf16(const uint16_t* W, int K, int N, uint16_t* WT, bool to_f16,
+                                 hipStream_t s);
+// kend[b] = 1 + last index j with mask[b][j] == 0, or 0 if every key is masked.
+hipError_t launch_mask_extent(const uint8_t* mask, int B, int T_k, int* kend, hipStream_t s);
+
+// ---- 16-bit MFMA GEMMs (C = A . Bt^T, both operands K-contiguous) -------
+struct QkvEpilogue {
+  int T;                 // rows of A per batch element (m = b*T + t)
+  int Tpad_q;            // padded sequence length of the q buffer
+  int Tpad_kv;           // padded sequence length of the k and vt buffers
+  int D, h, d_k;
+  int n_base;            // global column (0..3D) of GEMM column 0
+  const uint16_t* bias;  // (3D) bf16, or null
+  uint16_t* q;           // (B, h, Tpad_q, d_k) fp16 -- columns [0, D)
+  uint16_t* k;           // (B, h, Tpad_kv, d_k) fp16 -- columns [D, 2D)
+  uint16_t* vt;          // (B, h, d_k, Tpad_kv) fp16 -- columns [2D, 3D), transposed
+  float* early;          // (B, early_rows, 3D) fp32 copy of rows t < early_rows, or null
+  int early_rows;
+};
+// A: (M x K) bf16, Bt: (N x K) bf16.
+hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
+                           const QkvEpilogue& e, hipStream_t s);
+// A: (M x K) fp16, Bt: (N x K) fp16; Y (M x N) fp32 = A . Bt^T + bias (bf16, nullable).
+hipError_t launch_gemm_out(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
+                           const uint16_t* bias, float* Y, hipStream_t s);
+
+// ---- fused attention, fp16 operands, fp32 softmax state ------------------
+struct AttnF16Args {
+  const uint16_t* q;   // (B, h, Tqp, d_k) fp16
+  const uint16_t* k;   // (B, h, Tkp, d_k) fp16
+  const uint16_t* vt;  // (B, h, d_k, Tkp) fp16
+  uint16_t* o;         // (B, T_q, D) fp16, head i at columns [i*d_k, (i+1)*d_k)
+  const uint8_t* mask; // (B, T_k), nonzero = ignore, or null
+  const int* kend;     // (B) key extent from the mask, or null
+  int B, h, T_q, T_k, Tqp, Tkp, D, causal;
+};
+int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp must be a multiple)
+hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, hipStream_t s);
+
+// ---- fp32 path -----------------------------------------------------------
+// C[map(m)][n] = sum_k A[m][k] * B[k][n] + bias[n], with
+// map(m) = (m / rows_in) * rows_out + m % rows_in (identity when equal).
+// B and bias are fp32 or bf16 (b_bf16); bias may be null.
+hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B, int ldb, int N,
+                           bool b_bf16, const void* bias, float* C, int ldc, int rows_in,
+                           int rows_out, hipStream_t s);
+
+struct AttnF32Args {
+  const float* q; long q_bstride; int q_ld;    // q[b*q_bstride + t*q_ld + head*d_k + c]
+  const float* k; const float* v; long kv_bstride; int kv_ld;
+  float* o; long o_bstride; int o_ld;
+  const uint8_t* mask;                          // (B, mask_ld) nonzero = ignore, or null
+  int mask_ld;
+  int B, h, rows, T_k, causal;                 // rows = query rows evaluated (t = 0..rows-1)
+};
+hipError_t launch_attn_f32(const AttnF32Args& a, int d_k, hipStream_t s);
+
+}  // namespace mha

@@ -1,0 +1,373 @@
+// C ABI of the multi-head attention forward pass (declared in include/mha.h).
+//
+// Host-side only: argument validation, workspace layout and the launch
+// sequence. Every step of the computation runs in the kernels of prep.hip,
+// gemm16.hip, attn16.hip and fp32_path.hip.
+//
+// bf16 inputs (stages):
+//   prep       W_QKV -> W_QKV^T (bf16) and W_O -> W_O^T (fp16) so both MFMA
+//              operands of the projections are K-contiguous; key extent of
+//              the padding mask.
+//   qkv_proj   [Q|K|V] = X . W_QKV + b (cross-attention: Q from x_q,
+//              K and V from x_kv), fp32 accumulate, head split into fp16
+//              Q, K (B,h,T,d_k) and V^T (B,h,d_k,T).
+//   attention  fused masked softmax(QK^T/sqrt(d_k)) V -> O (B,T_q,D) fp16.
+//   out_proj   Y = O . W_O + b_O, fp32.
+//   early_rows causal only: rows t < 64 of every sequence, which average
+//              over at most 64 keys and therefore carry the largest outputs,
+//              are recomputed end to end in fp32 from fp32 copies of their
+//              Q/K/V and overwrite those rows of Y.
+// fp32 inputs: qkv_proj, attention and out_proj run the fp32 kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "../../include/mha.h"
+#include "kernels.h"
+
+struct mha_handle {
+  int D, h, d_k;
+  mha_dtype_t dtype;
+  // profiling state
+  int prof_max = 0;
+  int prof_calls = 0;
+  std::vector<hipEvent_t> prof_ev;   // prof_max * (MHA_NUM_STAGES + 1)
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int round_up(int x, int a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  // byte offsets into the workspace
+  size_t wqkvT = 0, woT = 0, q = 0, k = 0, vt = 0, o = 0, kend = 0, eqkv = 0, eo = 0;
+  size_t f_q = 0, f_kv = 0, f_o = 0;
+  size_t total = 0;
+  int Tqp = 0, Tkp = 0, R = 0;
+};
+
+Layout make_layout(const mha_handle* hd, int B, int T_q, int T_k) {
+  Layout L;
+  const size_t D = (size_t)hd->D;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, kAlign);
+    return at;
+  };
+  if (hd->dtype == MHA_BF16) {
+    const int bm = mha::attn_f16_block_m(hd->d_k);
+    L.Tqp = round_up(T_q, bm);
+    L.Tkp = round_up(T_k, bm);
+    L.R = std::min(mha::kEarlyRows, T_q);
+    L.wqkvT = take(3 * D * D * 2);
+    L.woT = take(D * D * 2);
+    L.q = take((size_t)B * L.Tqp * D * 2);
+    L.k = take((size_t)B * L.Tkp * D * 2);
+    L.vt = take((size_t)B * L.Tkp * D * 2);
+    L.o = take((size_t)B * T_q * D * 2);
+    L.kend = take((size_t)B * 4);
+    L.eqkv = take((size_t)B * L.R * 3 * D * 4);
+    L.eo = take((size_t)B * L.R * D * 4);
+  } else {
+    // One region: self-attention uses it as a single (B*T, 3D) buffer;
+    // cross-attention as Q (B*T_q, D) followed by [K|V] (B*T_k, 2D).
+    L.f_q = take((size_t)B * T_q * D * 4 + (size_t)B * T_k * 2 * D * 4);
+    L.f_kv = L.f_q + (size_t)B * T_q * D * 4;
+    L.f_o = take((size_t)B * T_q * D * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool sizes_ok(const mha_handle* hd, int B, int T_q, int T_k) {
+  if (B < 1 || T_q < 1 || T_k < 1) return false;
+  const long long D = hd->D;
+  // every row index (B*T) and every element count per buffer must fit the
+  // kernels' 32-bit row arithmetic
+  const long long rows = (long long)B * std::max(T_q, T_k);
+  if (rows > INT_MAX / 2) return false;
+  if ((long long)std::max(T_q, T_k) + 256 > INT_MAX / 4) return false;
+  (void)D;
+  return true;
+}
+
+#define MHA_HIP(call)                                   \
+  do {                                                  \
+    if ((call) != hipSuccess) return MHA_ERR_HIP;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+mha_status_t mha_create(mha_handle_t* out, int d_model, int num_heads, mha_dtype_t dtype) {
+  if (!out) return MHA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (d_model <= 0 || num_heads <= 0 || d_model % num_heads != 0) return MHA_ERR_INVALID_ARG;
+  if (dtype != MHA_F32 && dtype != MHA_BF16) return MHA_ERR_INVALID_ARG;
+  const int d_k = d_model / num_heads;
+  if ((d_k != 64 && d_k != 128) || d_model % 128 != 0) return MHA_ERR_UNSUPPORTED;
+  mha_handle* hd = new (std::nothrow) mha_handle();
+  if (!hd) return MHA_ERR_INVALID_ARG;
+  hd->D = d_model;
+  hd->h = num_heads;
+  hd->d_k = d_k;
+  hd->dtype = dtype;
+  *out = hd;
+  return MHA_OK;
+}
+
+size_t mha_workspace_size(mha_handle_t hd, int B, int T_q, int T_k) {
+  if (!hd || !sizes_ok(hd, B, T_q, T_k)) return 0;
+  return make_layout(hd, B, T_q, T_k).total;
+}
+
+mha_status_t mha_destroy(mha_handle_t hd) {
+  if (!hd) return MHA_OK;
+  for (hipEvent_t e : hd->prof_ev) (void)hipEventDestroy(e);
+  delete hd;
+  return MHA_OK;
+}
+
+const char* mha_status_string(mha_status_t s) {
+  switch (s) {
+    case MHA_OK: return "MHA_OK";
+    case MHA_ERR_INVALID_ARG: return "MHA_ERR_INVALID_ARG: invalid argument";
+    case MHA_ERR_UNSUPPORTED: return "MHA_ERR_UNSUPPORTED: configuration not supported by the kernels";
+    case MHA_ERR_WORKSPACE: return "MHA_ERR_WORKSPACE: workspace too small";
+    case MHA_ERR_HIP: return "MHA_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown mha_status_t";
+}
+
+const char* mha_stage_name(int s) {
+  static const char* names[MHA_NUM_STAGES] = {"prep", "qkv_proj", "attention", "out_proj",
+                                              "early_rows"};
+  return (s >= 0 && s < MHA_NUM_STAGES) ? names[s] : nullptr;
+}
+
+mha_status_t mha_profile_begin(mha_handle_t hd, int max_calls) {
+  if (!hd || max_calls < 1) return MHA_ERR_INVALID_ARG;
+  for (hipEvent_t e : hd->prof_ev) (void)hipEventDestroy(e);
+  hd->prof_ev.assign((size_t)max_calls * (MHA_NUM_STAGES + 1), nullptr);
+  for (auto& e : hd->prof_ev) MHA_HIP(hipEventCreate(&e));
+  hd->prof_max = max_calls;
+  hd->prof_calls = 0;
+  return MHA_OK;
+}
+
+mha_status_t mha_profile_end(mha_handle_t hd, float* stage_ms, int* n_calls) {
+  if (!hd || !stage_ms || !n_calls) return MHA_ERR_INVALID_ARG;
+  for (int s = 0; s < MHA_NUM_STAGES; ++s) stage_ms[s] = 0.0f;
+  const int n = hd->prof_calls;
+  *n_calls = n;
+  mha_status_t st = MHA_OK;
+  if (n > 0) {
+    const size_t per = MHA_NUM_STAGES + 1;
+    if (hipEventSynchronize(hd->prof_ev[(size_t)(n - 1) * per + MHA_NUM_STAGES]) != hipSuccess)
+      st = MHA_ERR_HIP;
+    for (int c = 0; c < n && st == MHA_OK; ++c)
+      for (int s = 0; s < MHA_NUM_STAGES; ++s) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, hd->prof_ev[c * per + s], hd->prof_ev[c * per + s + 1]) !=
+            hipSuccess) {
+          st = MHA_ERR_HIP;
+          break;
+        }
+        stage_ms[s] += ms / n;
+      }
+  }
+  for (hipEvent_t e : hd->prof_ev) (void)hipEventDestroy(e);
+  hd->prof_ev.clear();
+  hd->prof_max = 0;
+  hd->prof_calls = 0;
+  return st;
+}
+
+mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, const void* w_qkv,
+                         const void* b_qkv, const void* w_o, const void* b_o, int B, int T_q,
+                         int T_k, int causal, const unsigned char* key_padding_mask, float* y,
+                         void* workspace, size_t workspace_bytes, void* stream_) {
+  if (!hd) return MHA_ERR_INVALID_ARG;
+  if (!x_q || !w_qkv || !w_o || !y || !workspace) return MHA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return MHA_ERR_INVALID_ARG;
+  if (!x_kv && T_k != T_q) return MHA_ERR_INVALID_ARG;
+  if (causal && T_k != T_q) return MHA_ERR_INVALID_ARG;
+  if (!sizes_ok(hd, B, T_q, T_k)) return MHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_q, x_kv, w_qkv, b_qkv, w_o, b_o, y, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MHA_ERR_INVALID_ARG;
+  const Layout L = make_layout(hd, B, T_q, T_k);
+  if (workspace_bytes < L.total) return MHA_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int D = hd->D, h = hd->h, d_k = hd->d_k;
+  const bool cross = x_kv != nullptr;
+
+  // stage boundary events (measurement only)
+  hipEvent_t* ev = nullptr;
+  if (hd->prof_calls < hd->prof_max) {
+    ev = &hd->prof_ev[(size_t)hd->prof_calls * (MHA_NUM_STAGES + 1)];
+    ++hd->prof_calls;
+  }
+  auto mark = [&](int i) -> bool { return !ev || hipEventRecord(ev[i], s) == hipSuccess; };
+  if (!mark(0)) return MHA_ERR_HIP;
+
+  if (hd->dtype == MHA_BF16) {
+    const uint16_t* xq = static_cast<const uint16_t*>(x_q);
+    const uint16_t* xkv = static_cast<const uint16_t*>(x_kv);
+    uint16_t* wqkvT = reinterpret_cast<uint16_t*>(ws + L.wqkvT);
+    uint16_t* woT = reinterpret_cast<uint16_t*>(ws + L.woT);
+    uint16_t* q = reinterpret_cast<uint16_t*>(ws + L.q);
+    uint16_t* k = reinterpret_cast<uint16_t*>(ws + L.k);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
+    uint16_t* o = reinterpret_cast<uint16_t*>(ws + L.o);
+    int* kend = reinterpret_cast<int*>(ws + L.kend);
+    float* eqkv = reinterpret_cast<float*>(ws + L.eqkv);
+    float* eo = reinterpret_cast<float*>(ws + L.eo);
+    const uint16_t* bq = static_cast<const uint16_t*>(b_qkv);
+
+    // prep
+    MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_qkv), D, 3 * D, wqkvT,
+                                       false, s));
+    MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_o), D, D, woT, true, s));
+    if (key_padding_mask) MHA_HIP(mha::launch_mask_extent(key_padding_mask, B, T_k, kend, s));
+    if (!mark(1)) return MHA_ERR_HIP;
+
+    // qkv_proj
+    mha::QkvEpilogue e{};
+    e.Tpad_q = L.Tqp;
+    e.Tpad_kv = L.Tkp;
+    e.D = D;
+    e.h = h;
+    e.d_k = d_k;
+    e.bias = bq;
+    e.q = q;
+    e.k = k;
+    e.vt = vt;
+    e.early = causal ? eqkv : nullptr;
+    e.early_rows = L.R;
+    if (!cross) {
+      e.T = T_q;
+      e.n_base = 0;
+      MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wqkvT, 3 * D, e, s));
+    } else {
+      e.T = T_q;
+      e.n_base = 0;
+      MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wqkvT, D, e, s));
+      e.T = T_k;
+      e.n_base = D;
+      MHA_HIP(mha::launch_gemm_qkv(xkv, B * T_k, D, wqkvT + (size_t)D * D, 2 * D, e, s));
+    }
+    if (!mark(2)) return MHA_ERR_HIP;
+
+    // attention
+    mha::AttnF16Args a{};
+    a.q = q;
+    a.k = k;
+    a.vt = vt;
+    a.o = o;
+    a.mask = key_padding_mask;
+    a.kend = key_padding_mask ? kend : nullptr;
+    a.B = B;
+    a.h = h;
+    a.T_q = T_q;
+    a.T_k = T_k;
+    a.Tqp = L.Tqp;
+    a.Tkp = L.Tkp;
+    a.D = D;
+    a.causal = causal;
+    MHA_HIP(mha::launch_attn_f16(a, d_k, s));
+    if (!mark(3)) return MHA_ERR_HIP;
+
+    // out_proj
+    MHA_HIP(mha::launch_gemm_out(o, B * T_q, D, woT, D, static_cast<const uint16_t*>(b_o), y, s));
+    if (!mark(4)) return MHA_ERR_HIP;
+
+    // early_rows
+    if (causal) {
+      mha::AttnF32Args f{};
+      f.q = eqkv;
+      f.k = eqkv + D;
+      f.v = eqkv + 2 * D;
+      f.q_ld = f.kv_ld = 3 * D;
+      f.q_bstride = f.kv_bstride = (long)L.R * 3 * D;
+      f.o = eo;
+      f.o_ld = D;
+      f.o_bstride = (long)L.R * D;
+      f.mask = key_padding_mask;
+      f.mask_ld = T_k;
+      f.B = B;
+      f.h = h;
+      f.rows = L.R;
+      f.T_k = L.R;
+      f.causal = 1;
+      MHA_HIP(mha::launch_attn_f32(f, d_k, s));
+      MHA_HIP(mha::launch_gemm_f32(eo, D, B * L.R, D, w_o, D, D, true, b_o, y, D, L.R, T_q, s));
+    }
+    if (!mark(5)) return MHA_ERR_HIP;
+  } else {
+    const float* xq = static_cast<const float*>(x_q);
+    const float* xkv = static_cast<const float*>(x_kv);
+    const float* W = static_cast<const float*>(w_qkv);
+    const float* bqkv = static_cast<const float*>(b_qkv);
+    float* fq = reinterpret_cast<float*>(ws + L.f_q);
+    float* fkv = reinterpret_cast<float*>(ws + L.f_kv);
+    float* fo = reinterpret_cast<float*>(ws + L.f_o);
+    if (!mark(1)) return MHA_ERR_HIP;
+
+    mha::AttnF32Args f{};
+    if (!cross) {
+      // one (B*T, 3D) product; Q, K, V are column blocks of it
+      MHA_HIP(mha::launch_gemm_f32(xq, D, B * T_q, D, W, 3 * D, 3 * D, false, bqkv, fq, 3 * D,
+                                   B * T_q, B * T_q, s));
+      f.q = fq;
+      f.k = fq + D;
+      f.v = fq + 2 * D;
+      f.q_ld = f.kv_ld = 3 * D;
+      f.q_bstride = f.kv_bstride = (long)T_q * 3 * D;
+    } else {
+      MHA_HIP(mha::launch_gemm_f32(xq, D, B * T_q, D, W, 3 * D, D, false, bqkv, fq, D, B * T_q,
+                                   B * T_q, s));
+      MHA_HIP(mha::launch_gemm_f32(xkv, D, B * T_k, D, W + D, 3 * D, 2 * D, false,
+                                   bqkv ? bqkv + D : nullptr, fkv, 2 * D, B * T_k, B * T_k, s));
+      f.q = fq;
+      f.q_ld = D;
+      f.q_bstride = (long)T_q * D;
+      f.k = fkv;
+      f.v = fkv + D;
+      f.kv_ld = 2 * D;
+      f.kv_bstride = (long)T_k * 2 * D;
+    }
+    if (!mark(2)) return MHA_ERR_HIP;
+    f.o = fo;
+    f.o_ld = D;
+    f.o_bstride = (long)T_q * D;
+    f.mask = key_padding_mask;
+    f.mask_ld = T_k;
+    f.B = B;
+    f.h = h;
+    f.rows = T_q;
+    f.T_k = T_k;
+    f.causal = causal;
+    MHA_HIP(mha::launch_attn_f32(f, d_k, s));
+    if (!mark(3)) return MHA_ERR_HIP;
+    MHA_HIP(mha::launch_gemm_f32(fo, D, B * T_q, D, w_o, D, D, false, b_o, y, D, B * T_q, B * T_q,
+                                 s));
+    if (!mark(4) || !mark(5)) return MHA_ERR_HIP;
+  }
+  return MHA_OK;
+}
+
+}  // extern "C"
