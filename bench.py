@@ -81,27 +81,46 @@ def read_traffic(stage: str):
         return None
 
 
-def cpu_baseline(w, inp):
-    """fp64 oracle on batch element 0 of the workload, timed on this host."""
-    import numpy as np
+def cpu_baseline(w, inp, budget_s: float = 10.0):
+    """fp64 oracle on whole batch elements of the workload, one after another
+    until about ``budget_s`` seconds of host work, timed on this host."""
     from threadpoolctl import threadpool_info
     from mha_inputs import as_float64_numpy as f
     from oracle import mha_oracle
 
     mask = inp["key_padding_mask"]
-    t0 = time.perf_counter()
-    mha_oracle.mha_forward(
-        f(inp["x_q"][:1]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]), f(inp["b_o"]), w.h,
-        x_kv=None if inp["x_kv"] is None else f(inp["x_kv"][:1]), causal=w.causal,
-        key_padding_mask=None if mask is None else mask[:1].numpy())
-    dt = time.perf_counter() - t0
-    flops = w.flops() / w.B
+    wq, bq, wo, bo = f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]), f(inp["b_o"])
+    done, spent = 0, 0.0
+    while done < w.B and spent < budget_s:
+        b = slice(done, done + 1)
+        t0 = time.perf_counter()
+        mha_oracle.mha_forward(
+            f(inp["x_q"][b]), wq, bq, wo, bo, w.h,
+            x_kv=None if inp["x_kv"] is None else f(inp["x_kv"][b]), causal=w.causal,
+            key_padding_mask=None if mask is None else mask[b].numpy())
+        spent += time.perf_counter() - t0
+        done += 1
+    flops = w.flops() / w.B * done
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    del np
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"batch element 0 of {w.B} (all {w.T_q} query rows, all heads), "
-                      f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 numpy"}
+            "sample": f"{done} of {w.B} batch elements (all {w.T_q} query rows, all heads), "
+                      f"{flops / 1e9:.1f} GFLOP in {spent:.1f} s, fp64 numpy/BLAS"}
+
+
+def copy_calibration(torch, steps: int) -> int:
+    """A plain copy of known size: each launch reads and writes 1 GiB. Its
+    FETCH_SIZE / WRITE_SIZE counters give the scale from counter units to
+    HBM bytes."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(max(steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": max(steps, 1)}))
+    return 0
 
 
 def main() -> int:
@@ -111,6 +130,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (HBM counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -118,6 +139,8 @@ def main() -> int:
         return 2
 
     import torch
+    if args.copy_calibration:
+        return copy_calibration(torch, args.steps)
     import transformer_head_attention_amd as mha
     from mha_inputs import WORKLOADS, HEADLINE, make_inputs
 

@@ -115,6 +115,10 @@ mha_status_t mha_destroy(mha_handle_t handle);
 /* Static, human-readable name of a status code. */
 const char* mha_status_string(mha_status_t status);
 
+/* Description of the HIP error behind the most recent MHA_ERR_HIP returned
+ * on the calling thread ("no error" if there was none). Static storage. */
+const char* mha_hip_error_string(void);
+
 /* ---- Per-stage timing (measurement only; no effect on results) ----------
  * mha_profile_begin: subsequent mha_forward calls on this handle record HIP
  * events around each stage, for at most max_calls calls.

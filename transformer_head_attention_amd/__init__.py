@@ -22,6 +22,11 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
         "(hipcc, gfx950). The multi-head attention path has no CPU fallback.")
 
+# torch ships its own HIP runtime with the same soname (libamdhip64.so.7).
+# Loading torch first makes libmha.so bind to that one runtime, so device
+# pointers and streams handed over from torch are valid for the library.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 MHA_F32, MHA_BF16 = 0, 1
@@ -29,7 +34,8 @@ MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP
 MHA_NUM_STAGES = 5
 
 EXPORTED = ("mha_create", "mha_workspace_size", "mha_forward", "mha_destroy",
-            "mha_status_string", "mha_profile_begin", "mha_profile_end", "mha_stage_name")
+            "mha_status_string", "mha_hip_error_string", "mha_profile_begin", "mha_profile_end",
+            "mha_stage_name")
 
 _vp, _int, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _lib.mha_create.argtypes = [ctypes.POINTER(_vp), _int, _int, _int]
@@ -43,6 +49,8 @@ _lib.mha_destroy.argtypes = [_vp]
 _lib.mha_destroy.restype = _int
 _lib.mha_status_string.argtypes = [_int]
 _lib.mha_status_string.restype = ctypes.c_char_p
+_lib.mha_hip_error_string.argtypes = []
+_lib.mha_hip_error_string.restype = ctypes.c_char_p
 _lib.mha_profile_begin.argtypes = [_vp, _int]
 _lib.mha_profile_begin.restype = _int
 _lib.mha_profile_end.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_int)]
@@ -53,7 +61,10 @@ _lib.mha_stage_name.restype = ctypes.c_char_p
 
 class MHAError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {mha_status_string(status)}")
+        msg = f"{where}: {mha_status_string(status)}"
+        if status == MHA_ERR_HIP:
+            msg += f" ({mha_hip_error_string()})"
+        super().__init__(msg)
         self.status = status
 
 
@@ -66,6 +77,10 @@ def _check(status: int, where: str) -> None:
 
 def mha_status_string(status: int) -> str:
     return _lib.mha_status_string(int(status)).decode()
+
+
+def mha_hip_error_string() -> str:
+    return _lib.mha_hip_error_string().decode()
 
 
 def mha_stage_name(stage: int):

@@ -4,20 +4,25 @@
 //   o_i = sum_j softmax_j(q_i . k_j / sqrt(d_k) + M_ij) v_j
 // (itwiki "멀티 헤드 어텐션", 수식, eq. Attention; iamjaehka13.blog
 // "[Deep Learning 5] Attention의 내부 계산", §7-§13) without forming the
-// T_q x T_k score matrix. Keys are visited in tiles of 64; the softmax is
-// accumulated online: a running row maximum m and row sum l, with the partial
-// output rescaled by exp(m_old - m_new) whenever m grows. This is the same
-// softmax in exact arithmetic (the exp(-m) factor cancels between numerator
-// and denominator).
+// T_q x T_k score matrix. Keys are visited in tiles of 64 and the softmax is
+// accumulated online, against a per-row reference value `base`: the partial
+// numerator sum_j exp2(s_j - base) v_j and denominator sum_j exp2(s_j - base)
+// are carried across tiles, and both are multiplied by exp2(base_old -
+// base_new) when the reference moves. Any reference gives the same softmax
+// in exact arithmetic (the factor exp2(-base) cancels). The reference is the
+// first tile's row maximum and afterwards moves only when a score exceeds it
+// by more than 8 (log2 units), so exponentials stay in [0, 256] and most
+// tiles need no rescaling. Scores are produced in log2 units: Q is stored
+// pre-multiplied by log2(e)/sqrt(d_k), and the S accumulator starts at -base.
 //
 // Masks: key j > query i under the causal mask and keys flagged in the
 // padding mask (nonzero = ignore) get -inf, so their weight is exactly 0
 // (iamjaehka13.blog §9; molayo1419.me "MHA란 무엇인가?", trap 2). Key tiles
-// entirely in a wave's future are skipped; key tiles beyond the last unmasked
-// key of a batch element are never visited. A row with no unmasked key ends
-// with l = 0 and writes 0 * (1/0) = NaN (molayo1419.me, trap 3).
+// entirely in a query tile's future are skipped; key tiles beyond the last
+// unmasked key of a batch element are never visited. A row with no unmasked
+// key ends with l = 0 and writes 0 * (1/0) = NaN (molayo1419.me, trap 3).
 //
-// Layout of one wave's work: 32 query rows x one 64-key tile.
+// One wave's work per key tile: NQ x 32 query rows x 64 keys.
 //   S^T = K . Q^T with v_mfma_f32_32x32x16_f16: the K tile is the A operand
 //   (from LDS), Q^T the B operand (held in registers for the whole kernel).
 //   The result puts one query per lane column, so the row max and row sum
@@ -25,6 +30,13 @@
 //   O^T += V^T . P^T: P^T is repacked from the S^T accumulators in registers
 //   (fp16, round to nearest even) and used directly as the B operand; V^T
 //   comes from LDS in the same key order.
+//
+// Data movement: K and V^T tiles (and, with a padding mask, the tile's 64-bit
+// ignore mask) go from global memory straight into LDS with
+// global_load_lds_dwordx4, up to NS tiles in flight. Tiles are stored
+// unpadded with their 16-byte chunks XOR-swizzled by row so the MFMA operand
+// reads spread over the LDS banks. The waits are explicit (s_waitcnt vmcnt +
+// s_barrier): a __syncthreads() would wait for every outstanding load.
 #include <math.h>
 
 #include "device_common.h"
@@ -36,6 +48,7 @@ namespace {
 
 constexpr int BLOCK_N = 64;   // keys per tile
 constexpr int NWAVES = 4;
+constexpr int NT = NWAVES * 64;
 
 __device__ __forceinline__ int xcd_remap(int L, int total) {
   const int per = total / 8;
@@ -43,39 +56,43 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
   return (L % 8) * per + L / 8;
 }
 
-template <int DK>
-struct Lds {
-  static constexpr int KS = DK + 8;        // K tile row stride (16-bit elements)
-  static constexpr int VS = BLOCK_N + 8;   // V^T tile row stride
-  static constexpr int K_ELEMS = BLOCK_N * KS;
-  static constexpr int V_ELEMS = DK * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-};
-
-// Clear the fp16 elements of an 8-element chunk whose key index is >= limit.
-__device__ __forceinline__ u32x4 zero_from(u32x4 v, int first_key, int limit) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int k0 = first_key + 2 * e;
-    if (k0 >= limit) w[e] = 0u;
-    else if (k0 + 1 >= limit) w[e] &= 0xffffu;
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int DK, int NQ>
-__global__ void __launch_bounds__(NWAVES * 64)
+// s_waitcnt lgkmcnt(0) only (LDS reads and writes of this wave complete).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// Physical 16-byte chunk of logical chunk c in row `row` of a tile.
+template <int CHUNKS>
+__device__ __forceinline__ int swz(int row, int c) {
+  // 8 chunks per row (128-byte rows): pairs of rows share a 256-byte bank
+  // window, so rows 2r and 2r+1 rotate by the same amount.
+  return CHUNKS == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ (row & 15));
+}
+
+template <int DK, int NQ, int NS, bool HAS_MASK>
+__global__ void __launch_bounds__(NT)
 attn_f16_kernel(AttnF16Args a) {
   constexpr int BLOCK_M = NWAVES * 32 * NQ;
-  constexpr int NT = NWAVES * 64;
-  constexpr int K_PER_T = BLOCK_N * DK / 8 / NT;   // 16-byte chunks per thread
-  constexpr int V_PER_T = DK * BLOCK_N / 8 / NT;
+  constexpr int KCH = DK / 8;                       // 16-byte chunks per K row
+  constexpr int K_BYTES = BLOCK_N * DK * 2;
+  constexpr int V_BYTES = DK * BLOCK_N * 2;
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int K_LPT = K_BYTES / 16 / NT;          // DMA loads per thread per tile
+  constexpr int V_LPT = V_BYTES / 16 / NT;
+  constexpr int LPT = K_LPT + V_LPT + (HAS_MASK ? 1 : 0);
   constexpr int KSTEPS = DK / 16;
   constexpr int DT = DK / 32;
-  using L = Lds<DK>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
-  __shared__ uint64_t mbits[2];
+  static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
+  __shared__ __attribute__((aligned(16))) uint32_t mask_s[NS][2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 31, lh = lane >> 5;
@@ -95,6 +112,40 @@ attn_f16_kernel(AttnF16Args a) {
   const uint16_t* Vg = a.vt + (size_t)bh * DK * a.Tkp;
   const int qw0 = qblk * BLOCK_M + wave * 32 * NQ;
 
+  int kv_end = a.T_k;
+  if (HAS_MASK) kv_end = min(kv_end, a.kend[b]);
+  if (a.causal) kv_end = min(kv_end, qblk * BLOCK_M + BLOCK_M);
+  const int ntiles = kv_end > 0 ? (kv_end + BLOCK_N - 1) / BLOCK_N : 0;
+  const uint32_t* mbits_g = HAS_MASK ? a.mbits + (size_t)b * a.mbits_ld * 2 : nullptr;
+
+  // Issue the DMA loads of key tile `tile` into LDS stage `stage`. Lane
+  // chunk p of each wave-wide instruction lands at byte 16*p of the wave's
+  // contiguous 1 KiB window; the lane fetches the global chunk that the
+  // swizzled layout places there.
+  auto issue = [&](int tile, int stage) __attribute__((always_inline)) {
+    const int k0 = tile * BLOCK_N;
+    uint8_t* kst = smem + stage * STAGE;
+    uint8_t* vst = kst + K_BYTES;
+#pragma unroll
+    for (int i = 0; i < K_LPT; ++i) {
+      const int p = i * NT + tid, row = p / KCH, c = swz<KCH>(row, p % KCH);
+      __builtin_amdgcn_global_load_lds(Kg + (size_t)(k0 + row) * DK + c * 8,
+                                       kst + (i * NT + wave * 64) * 16, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < V_LPT; ++i) {
+      const int p = i * NT + tid, row = p / 8, c = swz<8>(row, p % 8);
+      __builtin_amdgcn_global_load_lds(Vg + (size_t)row * a.Tkp + k0 + c * 8,
+                                       vst + (i * NT + wave * 64) * 16, 16, 0, 0);
+    }
+    if (HAS_MASK) {
+      // The tile's two mask dwords; every wave writes the same bytes.
+      if (lane < 2)
+        __builtin_amdgcn_global_load_lds(mbits_g + tile * 2 + lane, &mask_s[stage][0], 4, 0, 0);
+    }
+  };
+
+  // Q tile in registers (B operand of S^T = K . Q^T); rows past T_q are zero.
   u32x4 qreg[NQ][KSTEPS];
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
@@ -107,10 +158,12 @@ attn_f16_kernel(AttnF16Args a) {
   }
 
   f32x16_t o[NQ][DT];
-  float m_run[NQ], l_run[NQ];
+  float base[NQ], l_run[NQ];
+  bool seen[NQ];   // has this lane's query met an unmasked key yet
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
-    m_run[qi] = -INFINITY;
+    base[qi] = 0.0f;
+    seen[qi] = false;
     l_run[qi] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -118,109 +171,118 @@ attn_f16_kernel(AttnF16Args a) {
       for (int r = 0; r < 16; ++r) o[qi][dt][r] = 0.0f;
   }
 
-  int kv_end = a.T_k;
-  if (a.kend) kv_end = min(kv_end, a.kend[b]);
-  if (a.causal) kv_end = min(kv_end, qblk * BLOCK_M + BLOCK_M);
-  const int ntiles = kv_end > 0 ? (kv_end + BLOCK_N - 1) / BLOCK_N : 0;
-  const bool has_mask = a.mask != nullptr;
-  const uint8_t* maskb = has_mask ? a.mask + (size_t)b * a.T_k : nullptr;
-  // log2(e) / sqrt(d_k): scores are exponentiated with exp2.
-  const float sl2 = 1.4426950408889634f / sqrtf((float)DK);
-
-  u32x4 rk[K_PER_T], rv[V_PER_T];
-  uint64_t rbits = 0;
-  auto gload = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * NT, row = c / (DK / 8), col = (c % (DK / 8)) * 8;
-      rk[i] = *reinterpret_cast<const u32x4*>(Kg + (size_t)(k0 + row) * DK + col);
-    }
-    const bool tail = k0 + BLOCK_N > a.T_k;
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int c = tid + i * NT, row = c / (BLOCK_N / 8), col = (c % (BLOCK_N / 8)) * 8;
-      rv[i] = *reinterpret_cast<const u32x4*>(Vg + (size_t)row * a.Tkp + k0 + col);
-      if (tail) rv[i] = zero_from(rv[i], k0 + col, a.T_k);
-    }
-    if (wave == 0) {
-      const int key = k0 + lane;
-      const bool ignore = key >= a.T_k || (has_mask && maskb[key] != 0);
-      rbits = __ballot(ignore);
-    }
-  };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* Ks = smem + buf * L::STAGE;
-    uint16_t* Vs = Ks + L::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * NT, row = c / (DK / 8), col = (c % (DK / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + row * L::KS + col) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int c = tid + i * NT, row = c / (BLOCK_N / 8), col = (c % (BLOCK_N / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Vs + row * L::VS + col) = rv[i];
-    }
-    if (tid == 0) mbits[buf] = rbits;
-  };
-
-  if (ntiles > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) issue(t, t);
 
   for (int it = 0; it < ntiles; ++it) {
     const int k0 = it * BLOCK_N;
-    const int buf = it & 1;
-    if (it + 1 < ntiles) gload(k0 + BLOCK_N);
-    const uint16_t* Ks = smem + buf * L::STAGE;
-    const uint16_t* Vs = Ks + L::K_ELEMS;
-    const uint64_t bits = mbits[buf] >> (4 * lh);
-    const bool tile_masked = has_mask || (k0 + BLOCK_N > a.T_k);
+    const int stage = it % NS;
+    // Tile `it` is complete once at most the loads of the younger tiles
+    // already issued (up to NS-2 of them) are outstanding.
+    const int younger = min(NS - 2, ntiles - 1 - it);
+    if (younger >= 2) wait_vmcnt<2 * LPT>();
+    else if (younger == 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();   // every wave's part of tile `it` has landed
+    // The stage read in the previous iteration is free again.
+    if (it + NS - 1 < ntiles) issue(it + NS - 1, (it + NS - 1) % NS);
 
+    const uint8_t* Ks = smem + stage * STAGE;
+    const uint8_t* Vs = Ks + K_BYTES;
+    const bool tail = k0 + BLOCK_N > a.T_k;
+    if (tail) {
+      // Keys >= T_k of the last tile hold no data: clear their V^T columns
+      // (their weights are exactly 0, and 0 * garbage could be NaN).
+      uint8_t* vw = smem + stage * STAGE + K_BYTES;
+      for (int p = tid; p < DK * 8; p += NT) {
+        const int row = p / 8, c = p % 8;
+        u32x4* chunk = reinterpret_cast<u32x4*>(vw + (row * 8 + swz<8>(row, c)) * 16);
+        const u32x4 v = *chunk;
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + c * 8 + 2 * e;
+          if (key >= a.T_k) w[e] = 0u;
+          else if (key + 1 >= a.T_k) w[e] &= 0xffffu;
+        }
+        *chunk = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+    }
+    uint64_t bits = 0;
+    if (HAS_MASK)
+      bits = (((uint64_t)mask_s[stage][1] << 32) | mask_s[stage][0]) >> (4 * lh);
+    const bool masked_tile = HAS_MASK || tail;
+
+    // Phase 1: S'^T = K . Q^T - base for every live query tile.
+    f32x16_t s[NQ][2];
+    bool live[NQ];
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
       const int q_lo = qw0 + qi * 32;
-      if (a.causal && k0 > q_lo + 31) continue;   // whole tile in this wave's future
-
-      f32x16_t s[2];
+      live[qi] = !(a.causal && k0 > q_lo + 31);
+      if (!live[qi]) continue;
+      const float init = -base[qi];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kh][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) s[qi][kh][r] = init;
+        const int row = kh * 32 + lq;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-          const u32x4 kf =
-              *reinterpret_cast<const u32x4*>(Ks + (kh * 32 + lq) * L::KS + ks * 16 + lh * 8);
-          s[kh] = mfma32x32x16<F16>(kf, qreg[qi][ks], s[kh]);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(
+              Ks + (row * KCH + swz<KCH>(row, 2 * ks + lh)) * 16);
+          s[qi][kh] = mfma32x32x16<F16>(kf, qreg[qi][ks], s[qi][kh]);
         }
       }
+    }
 
+    // Phase 2 (per query tile): mask, lazy reference update, P = exp2(S'),
+    // then O^T += V^T . P^T.
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+      if (!live[qi]) continue;
+      const int q_lo = qw0 + qi * 32;
       // Key of accumulator element (kh, r): k0 + kh*32 + 8*(r/4) + 4*lh + r%4.
       const bool diag = a.causal && (k0 + BLOCK_N - 1 > q_lo);
-      if (diag || tile_masked) {
+      if (diag || masked_tile) {
         const int lim = q_lo + lq - k0 - 4 * lh;   // causal: masked iff rel > lim
+        const int kmax = a.T_k - k0 - 4 * lh;      // past T_k: masked iff rel >= kmax
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rel = kh * 32 + 8 * (r >> 2) + (r & 3);
-            const bool ign = (tile_masked && ((bits >> rel) & 1ull)) || (a.causal && rel > lim);
-            if (ign) s[kh][r] = -INFINITY;
+            bool ign = (a.causal && rel > lim) || rel >= kmax;
+            if (HAS_MASK) ign = ign || ((bits >> rel) & 1ull);
+            if (ign) s[qi][kh][r] = -INFINITY;
           }
       }
 
-      float mx = s[0][0];
+      float mx = s[qi][0][0];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qi][kh][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qi], mx);
-      const float base = (m_new == -INFINITY) ? 0.0f : m_new * sl2;
-      const float alpha = __builtin_amdgcn_exp2f(__builtin_fmaf(m_run[qi], sl2, -base));
-      m_run[qi] = m_new;
+      const bool first = !seen[qi] && mx != -INFINITY;
+      const float shift = first ? mx : (mx > 8.0f ? mx : 0.0f);
+      if (__ballot(shift != 0.0f)) {
+        const float alpha = seen[qi] ? __builtin_amdgcn_exp2f(-shift) : 1.0f;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[qi][kh][r] -= shift;
+        l_run[qi] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[qi][dt][r] *= alpha;
+        base[qi] += shift;
+      }
+      seen[qi] = seen[qi] || first;
 
       float rs = 0.0f;
       u32x4 pf[4];
@@ -229,33 +291,29 @@ attn_f16_kernel(AttnF16Args a) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c >> 1][(c & 1) * 8 + e], sl2, -base));
+          p[e] = __builtin_amdgcn_exp2f(s[qi][c >> 1][(c & 1) * 8 + e]);
           rs += p[e];
         }
         pf[c] = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]),
                       pack_f16x2(p[4], p[5]), pack_f16x2(p[6], p[7])};
       }
-      l_run[qi] = __builtin_fmaf(l_run[qi], alpha, rs);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[qi][dt][r] *= alpha;
+      l_run[qi] += rs;
 
       // P^T fragment c covers keys c*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}; V^T
-      // supplies the same keys for its row d.
+      // supplies the same keys for its row d: 8-byte halves of chunks 2c and
+      // 2c+1.
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) {
+        const int row = dt * 32 + lq;
+        const uint8_t* vrow = Vs + row * 128 + lh * 8;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint16_t* vp = Vs + (dt * 32 + lq) * L::VS + c * 16 + lh * 4;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + swz<8>(row, 2 * c) * 16);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + swz<8>(row, 2 * c + 1) * 16);
           o[qi][dt] = mfma32x32x16<F16>(u32x4{lo.x, lo.y, hi.x, hi.y}, pf[c], o[qi][dt]);
         }
+      }
     }
-
-    if (it + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // O = acc / l; head `head` occupies columns [head*DK, (head+1)*DK) of (B, T_q, D).
@@ -280,22 +338,65 @@ attn_f16_kernel(AttnF16Args a) {
   }
 }
 
-constexpr int kNQ = 1;
+// Query tiles (of 32 rows) per wave and pipeline depth per head size.
+#ifndef MHA_ATTN_NQ64
+#define MHA_ATTN_NQ64 1
+#endif
+#ifndef MHA_ATTN_NS64
+#define MHA_ATTN_NS64 4
+#endif
+#ifndef MHA_ATTN_NS128
+#define MHA_ATTN_NS128 3
+#endif
+constexpr int nq_for(int d_k) { return d_k == 64 ? MHA_ATTN_NQ64 : 1; }
+
+template <int DK, int NS>
+hipError_t launch_dk(const AttnF16Args& a, int total, hipStream_t s) {
+  if (a.mbits)
+    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, true>), dim3(total), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, false>), dim3(total), dim3(NT), 0, s,
+                       a);
+  return hipGetLastError();
+}
+
+// Per 64-key tile of each batch element, a 64-bit mask of the keys to
+// ignore: padding-mask nonzero, or index >= T_k. One thread per tile.
+__global__ void __launch_bounds__(256)
+mask_bits_kernel(const uint8_t* __restrict__ mask, int B, int T_k, int ntk,
+                 uint32_t* __restrict__ bits) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * ntk) return;
+  const int b = i / ntk, tile = i - b * ntk;
+  uint32_t w[2] = {0u, 0u};
+  for (int j = 0; j < BLOCK_N; ++j) {
+    const int key = tile * BLOCK_N + j;
+    const bool ign = key >= T_k || mask[(size_t)b * T_k + key] != 0;
+    if (ign) w[j >> 5] |= 1u << (j & 31);
+  }
+  bits[(size_t)i * 2] = w[0];
+  bits[(size_t)i * 2 + 1] = w[1];
+}
 
 }  // namespace
 
-int attn_f16_block_m(int /*d_k*/) { return NWAVES * 32 * kNQ; }
+int attn_f16_block_m(int d_k) { return NWAVES * 32 * nq_for(d_k); }
+
+int attn_mask_tiles(int T_k) { return (T_k + BLOCK_N - 1) / BLOCK_N; }
+
+hipError_t launch_mask_bits(const uint8_t* mask, int B, int T_k, uint32_t* bits, hipStream_t s) {
+  const int ntk = attn_mask_tiles(T_k);
+  hipLaunchKernelGGL(mask_bits_kernel, dim3((B * ntk + 255) / 256), dim3(256), 0, s, mask, B, T_k,
+                     ntk, bits);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, hipStream_t s) {
   const int bm = attn_f16_block_m(d_k);
   const int total = (a.Tqp / bm) * a.h * a.B;
-  if (d_k == 64)
-    hipLaunchKernelGGL((attn_f16_kernel<64, kNQ>), dim3(total), dim3(NWAVES * 64), 0, s, a);
-  else if (d_k == 128)
-    hipLaunchKernelGGL((attn_f16_kernel<128, kNQ>), dim3(total), dim3(NWAVES * 64), 0, s, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (d_k == 64) return launch_dk<64, MHA_ATTN_NS64>(a, total, s);
+  if (d_k == 128) return launch_dk<128, MHA_ATTN_NS128>(a, total, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mha

@@ -8,7 +8,7 @@
 //  * attn_f32: softmax(q . k / sqrt(d_k) + M) v row by row in fp32
 //    (same page, 수식; iamjaehka13.blog "[Deep Learning 5]", §7-§13). Each
 //    query row is shared by d_k/16 lanes that each own 16 of its dimensions;
-//    keys are staged through LDS in chunks of 32 and folded into a running
+//    keys are staged through LDS in chunks of 64 and folded into a running
 //    max / running sum.
 #include <math.h>
 
@@ -100,13 +100,14 @@ gemm_f32_kernel(const float* __restrict__ A, int lda, int M, int K, const void* 
   }
 }
 
-constexpr int KC = 32;   // keys per LDS chunk
+constexpr int KC = 64;           // keys per LDS chunk
+constexpr int ATTN32_NT = 256;   // threads per workgroup
 
 template <int DK>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(ATTN32_NT)
 attn_f32_kernel(AttnF32Args a) {
-  constexpr int TPR = DK / 16;    // lanes per query row
-  constexpr int RPB = 64 / TPR;   // query rows per workgroup
+  constexpr int TPR = DK / 16;           // lanes per query row
+  constexpr int RPB = ATTN32_NT / TPR;   // query rows per workgroup
   __shared__ __attribute__((aligned(16))) float Ks[KC][DK];
   __shared__ __attribute__((aligned(16))) float Vs[KC][DK];
 
@@ -133,7 +134,7 @@ attn_f32_kernel(AttnF32Args a) {
 
   for (int j0 = 0; j0 < kend; j0 += KC) {
     __syncthreads();
-    for (int idx = tid; idx < KC * DK / 4; idx += 64) {
+    for (int idx = tid; idx < KC * DK / 4; idx += ATTN32_NT) {
       const int key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4, j = j0 + key;
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
       if (j < a.T_k) {
@@ -199,11 +200,11 @@ hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B,
 
 hipError_t launch_attn_f32(const AttnF32Args& a, int d_k, hipStream_t s) {
   if (d_k == 64) {
-    dim3 grid((a.rows + 15) / 16, a.h, a.B);
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, a);
+    dim3 grid((a.rows + 63) / 64, a.h, a.B);
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(ATTN32_NT), 0, s, a);
   } else if (d_k == 128) {
-    dim3 grid((a.rows + 7) / 8, a.h, a.B);
-    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, a);
+    dim3 grid((a.rows + 31) / 32, a.h, a.B);
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(ATTN32_NT), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -181,12 +181,13 @@ struct QkvEpi {
           } else {
             uint16_t* base = which == 0 ? e.q : e.k;
             const int tpad = which == 0 ? e.Tpad_q : e.Tpad_kv;
+            const float sc = which == 0 ? e.q_scale : 1.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int m = mf + r;
               if (m >= M) break;
               const int b = m / e.T, t = m - b * e.T;
-              base[(((size_t)b * e.h + head) * tpad + t) * d_k + c] = float_to_f16_bits(v[r]);
+              base[(((size_t)b * e.h + head) * tpad + t) * d_k + c] = float_to_f16_bits(v[r] * sc);
             }
           }
         }
@@ -218,6 +219,59 @@ struct OutEpi {
   }
 };
 
+// Output projection of the first rows of each causal sequence, from their
+// fp32 attention output: Y[b*T_q + t] = O32[b*R + t] . W_O + b_O for t < R.
+// Each fp32 value x is split into fp16 hi = fp16(x) and lo = fp16(x - hi), and
+// hi . W + lo . W is accumulated in fp32 on the fp16 MFMA, which keeps about
+// 22 significant bits of x. A workgroup owns a 32 x 32 tile of Y; its four
+// waves take a quarter of K each and are summed through LDS in a fixed order.
+__global__ void __launch_bounds__(256)
+early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __restrict__ WoT,
+                 int N, const uint16_t* __restrict__ bias, float* __restrict__ Y, int R, int T_q) {
+  __shared__ f32x16_t red[3][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int kw = K / 4, kbeg = wave * kw;
+  const int row = min(m0 + (lane & 31), M - 1);
+  const float* ap = O32 + (size_t)row * K + (lane >> 5) * 8;
+  const uint16_t* bp = WoT + (size_t)(n0 + (lane & 31)) * K + (lane >> 5) * 8;
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll 4
+  for (int k = kbeg; k < kbeg + kw; k += 16) {
+    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(ap + k);
+    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(ap + k + 4);
+    const u32x4 bf = *reinterpret_cast<const u32x4*>(bp + k);
+    const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 h0 = static_cast<_Float16>(av[2 * e]);
+      const _Float16 h1 = static_cast<_Float16>(av[2 * e + 1]);
+      hi[e] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
+      lo[e] = pack_f16x2(av[2 * e] - static_cast<float>(h0), av[2 * e + 1] - static_cast<float>(h1));
+    }
+    acc = mfma32x32x16<F16>(u32x4{hi[0], hi[1], hi[2], hi[3]}, bf, acc);
+    acc = mfma32x32x16<F16>(u32x4{lo[0], lo[1], lo[2], lo[3]}, bf, acc);
+  }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) acc += red[w][lane];
+  const int n = n0 + (lane & 31);
+  const float bv = load_bias_bf16(bias, n);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (m < M) {
+      const int bb = m / R, t = m - bb * R;
+      Y[((size_t)bb * T_q + t) * N + n] = acc[r] + bv;
+    }
+  }
+}
+
 using QkvCfg = Cfg<128, 128, 64, 64>;
 using OutCfg = Cfg<128, 128, 64, 64>;
 
@@ -230,6 +284,13 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
   QkvEpi epi{e};
   hipLaunchKernelGGL((gemm16_kernel<C, BF16, QkvEpi>), dim3(tiles), dim3(C::NT), 0, s, A, Bt, M,
                      N, K, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
+                            const uint16_t* bias, float* Y, int R, int T_q, hipStream_t s) {
+  dim3 grid(N / 32, (M + 31) / 32);
+  hipLaunchKernelGGL(early_out_kernel, grid, dim3(256), 0, s, O32, M, K, WoT, N, bias, Y, R, T_q);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ struct QkvEpilogue {
   uint16_t* vt;          // (B, h, d_k, Tpad_kv) fp16 -- columns [2D, 3D), transposed
   float* early;          // (B, early_rows, 3D) fp32 copy of rows t < early_rows, or null
   int early_rows;
+  float q_scale;         // multiplies the fp16 Q (the fp32 early copy is unscaled)
 };
 // A: (M x K) bf16, Bt: (N x K) bf16.
 hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
@@ -40,17 +41,26 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
 hipError_t launch_gemm_out(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
                            const uint16_t* bias, float* Y, hipStream_t s);
 
+// Early causal rows: Y[b*T_q + t] = O32[b*R + t] . W_O + bias for t < R, from
+// fp32 O32 (M = B*R rows x K) and fp16 W_O^T (N x K); N % 32 == 0, K % 64 == 0.
+hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
+                            const uint16_t* bias, float* Y, int R, int T_q, hipStream_t s);
+
 // ---- fused attention, fp16 operands, fp32 softmax state ------------------
 struct AttnF16Args {
-  const uint16_t* q;   // (B, h, Tqp, d_k) fp16
+  const uint16_t* q;   // (B, h, Tqp, d_k) fp16, pre-multiplied by log2(e)/sqrt(d_k)
   const uint16_t* k;   // (B, h, Tkp, d_k) fp16
   const uint16_t* vt;  // (B, h, d_k, Tkp) fp16
   uint16_t* o;         // (B, T_q, D) fp16, head i at columns [i*d_k, (i+1)*d_k)
-  const uint8_t* mask; // (B, T_k), nonzero = ignore, or null
-  const int* kend;     // (B) key extent from the mask, or null
+  const uint32_t* mbits;  // (B, mbits_ld, 2) ignore bitmask per 64-key tile, or null
+  int mbits_ld;           // 64-key tiles per batch element (attn_mask_tiles(T_k))
+  const int* kend;     // (B) key extent from the mask; read only with mbits
   int B, h, T_q, T_k, Tqp, Tkp, D, causal;
 };
-int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp must be a multiple)
+int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp, Tkp must be multiples)
+int attn_mask_tiles(int T_k);    // 64-key tiles covering T_k
+// bits[b][tile] (two uint32): bit j set if key tile*64+j is masked or >= T_k.
+hipError_t launch_mask_bits(const uint8_t* mask, int B, int T_k, uint32_t* bits, hipStream_t s);
 hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, hipStream_t s);
 
 // ---- fp32 path -----------------------------------------------------------

@@ -15,13 +15,15 @@
 //   out_proj   Y = O . W_O + b_O, fp32.
 //   early_rows causal only: rows t < 64 of every sequence, which average
 //              over at most 64 keys and therefore carry the largest outputs,
-//              are recomputed end to end in fp32 from fp32 copies of their
-//              Q/K/V and overwrite those rows of Y.
+//              are recomputed from fp32 copies of their Q/K/V: attention in
+//              fp32, then the output projection with the fp32 result split
+//              into fp16 hi + lo parts; they overwrite those rows of Y.
 // fp32 inputs: qkv_proj, attention and out_proj run the fp32 kernels.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstdint>
 #include <new>
 #include <vector>
@@ -47,7 +49,8 @@ int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
 struct Layout {
   // byte offsets into the workspace
-  size_t wqkvT = 0, woT = 0, q = 0, k = 0, vt = 0, o = 0, kend = 0, eqkv = 0, eo = 0;
+  size_t wqkvT = 0, woT = 0, q = 0, k = 0, vt = 0, o = 0, kend = 0, mbits = 0, eqkv = 0,
+         eo = 0;
   size_t f_q = 0, f_kv = 0, f_o = 0;
   size_t total = 0;
   int Tqp = 0, Tkp = 0, R = 0;
@@ -74,6 +77,7 @@ Layout make_layout(const mha_handle* hd, int B, int T_q, int T_k) {
     L.vt = take((size_t)B * L.Tkp * D * 2);
     L.o = take((size_t)B * T_q * D * 2);
     L.kend = take((size_t)B * 4);
+    L.mbits = take((size_t)B * mha::attn_mask_tiles(T_k) * 8);
     L.eqkv = take((size_t)B * L.R * 3 * D * 4);
     L.eo = take((size_t)B * L.R * D * 4);
   } else {
@@ -101,9 +105,15 @@ bool sizes_ok(const mha_handle* hd, int B, int T_q, int T_k) {
   return true;
 }
 
-#define MHA_HIP(call)                                   \
-  do {                                                  \
-    if ((call) != hipSuccess) return MHA_ERR_HIP;      \
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+#define MHA_HIP(call)                       \
+  do {                                      \
+    const hipError_t e_ = (call);           \
+    if (e_ != hipSuccess) {                 \
+      g_last_hip_error = e_;                \
+      return MHA_ERR_HIP;                   \
+    }                                       \
   } while (0)
 
 }  // namespace
@@ -149,6 +159,8 @@ const char* mha_status_string(mha_status_t s) {
   }
   return "unknown mha_status_t";
 }
+
+const char* mha_hip_error_string(void) { return hipGetErrorString(g_last_hip_error); }
 
 const char* mha_stage_name(int s) {
   static const char* names[MHA_NUM_STAGES] = {"prep", "qkv_proj", "attention", "out_proj",
@@ -221,7 +233,15 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     ev = &hd->prof_ev[(size_t)hd->prof_calls * (MHA_NUM_STAGES + 1)];
     ++hd->prof_calls;
   }
-  auto mark = [&](int i) -> bool { return !ev || hipEventRecord(ev[i], s) == hipSuccess; };
+  auto mark = [&](int i) -> bool {
+    if (!ev) return true;
+    const hipError_t e = hipEventRecord(ev[i], s);
+    if (e != hipSuccess) g_last_hip_error = e;
+    return e == hipSuccess;
+  };
+  // Launch errors are read back with hipGetLastError: clear whatever an
+  // earlier, unrelated call left there so it is not reported as ours.
+  (void)hipGetLastError();
   if (!mark(0)) return MHA_ERR_HIP;
 
   if (hd->dtype == MHA_BF16) {
@@ -234,6 +254,7 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
     uint16_t* o = reinterpret_cast<uint16_t*>(ws + L.o);
     int* kend = reinterpret_cast<int*>(ws + L.kend);
+    uint32_t* mbits = reinterpret_cast<uint32_t*>(ws + L.mbits);
     float* eqkv = reinterpret_cast<float*>(ws + L.eqkv);
     float* eo = reinterpret_cast<float*>(ws + L.eo);
     const uint16_t* bq = static_cast<const uint16_t*>(b_qkv);
@@ -242,7 +263,10 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_qkv), D, 3 * D, wqkvT,
                                        false, s));
     MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_o), D, D, woT, true, s));
-    if (key_padding_mask) MHA_HIP(mha::launch_mask_extent(key_padding_mask, B, T_k, kend, s));
+    if (key_padding_mask) {
+      MHA_HIP(mha::launch_mask_extent(key_padding_mask, B, T_k, kend, s));
+      MHA_HIP(mha::launch_mask_bits(key_padding_mask, B, T_k, mbits, s));
+    }
     if (!mark(1)) return MHA_ERR_HIP;
 
     // qkv_proj
@@ -258,6 +282,9 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     e.vt = vt;
     e.early = causal ? eqkv : nullptr;
     e.early_rows = L.R;
+    // Q is stored pre-multiplied by log2(e)/sqrt(d_k): the attention kernel
+    // then exponentiates scores with exp2 directly.
+    e.q_scale = (float)(1.4426950408889634 / std::sqrt((double)d_k));
     if (!cross) {
       e.T = T_q;
       e.n_base = 0;
@@ -278,7 +305,8 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     a.k = k;
     a.vt = vt;
     a.o = o;
-    a.mask = key_padding_mask;
+    a.mbits = key_padding_mask ? mbits : nullptr;
+    a.mbits_ld = mha::attn_mask_tiles(T_k);
     a.kend = key_padding_mask ? kend : nullptr;
     a.B = B;
     a.h = h;
@@ -314,7 +342,8 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
       f.T_k = L.R;
       f.causal = 1;
       MHA_HIP(mha::launch_attn_f32(f, d_k, s));
-      MHA_HIP(mha::launch_gemm_f32(eo, D, B * L.R, D, w_o, D, D, true, b_o, y, D, L.R, T_q, s));
+      MHA_HIP(mha::launch_early_out(eo, B * L.R, D, woT, D, static_cast<const uint16_t*>(b_o), y,
+                                    L.R, T_q, s));
     }
     if (!mark(5)) return MHA_ERR_HIP;
   } else {
