@@ -20,6 +20,11 @@ LIB = os.path.join(PKG, "libmha.so")
 
 SOURCES = ["mha_api.hip", "prep.hip", "gemm16.hip", "attn16.hip", "fp32_path.hip"]
 
+# Per-source extra flags. The attention kernel keeps its MFMA accumulators in
+# ordinary VGPRs (no AGPR copies around the softmax); the large GEMM tiles need
+# the AGPR file for their 256 accumulators per lane.
+EXTRA = {"attn16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -52,7 +57,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

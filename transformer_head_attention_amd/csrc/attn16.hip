@@ -28,8 +28,9 @@
 //   The result puts one query per lane column, so the row max and row sum
 //   over keys are reductions inside a lane plus one exchange with lane l^32.
 //   O^T += V^T . P^T: P^T is repacked from the S^T accumulators in registers
-//   (fp16, round to nearest even) and used directly as the B operand; V^T
-//   comes from LDS in the same key order.
+//   (fp16, round to nearest even) and used directly as the B operand. V^T
+//   rows are stored with each 16-key group ordered {0-3, 8-11, 4-7, 12-15},
+//   so the keys a lane half needs for one k-step form one 16-byte chunk.
 //
 // Data movement: K and V^T tiles (and, with a padding mask, the tile's 64-bit
 // ignore mask) go from global memory straight into LDS with
@@ -129,19 +130,19 @@ attn_f16_kernel(AttnF16Args a) {
 #pragma unroll
     for (int i = 0; i < K_LPT; ++i) {
       const int p = i * NT + tid, row = p / KCH, c = swz<KCH>(row, p % KCH);
-      __builtin_amdgcn_global_load_lds(Kg + (size_t)(k0 + row) * DK + c * 8,
-                                       kst + (i * NT + wave * 64) * 16, 16, 0, 0);
+      lds_dma16(Kg + (size_t)(k0 + row) * DK + c * 8,
+                kst + (i * NT + wave * 64) * 16);
     }
 #pragma unroll
     for (int i = 0; i < V_LPT; ++i) {
       const int p = i * NT + tid, row = p / 8, c = swz<8>(row, p % 8);
-      __builtin_amdgcn_global_load_lds(Vg + (size_t)row * a.Tkp + k0 + c * 8,
-                                       vst + (i * NT + wave * 64) * 16, 16, 0, 0);
+      lds_dma16(Vg + (size_t)row * a.Tkp + k0 + c * 8,
+                vst + (i * NT + wave * 64) * 16);
     }
     if (HAS_MASK) {
       // The tile's two mask dwords; every wave writes the same bytes.
       if (lane < 2)
-        __builtin_amdgcn_global_load_lds(mbits_g + tile * 2 + lane, &mask_s[stage][0], 4, 0, 0);
+        lds_dma4(mbits_g + tile * 2 + lane, &mask_s[stage][0]);
     }
   };
 
@@ -193,7 +194,8 @@ attn_f16_kernel(AttnF16Args a) {
     const bool tail = k0 + BLOCK_N > a.T_k;
     if (tail) {
       // Keys >= T_k of the last tile hold no data: clear their V^T columns
-      // (their weights are exactly 0, and 0 * garbage could be NaN).
+      // (their weights are exactly 0, and 0 * garbage could be NaN). Chunk c
+      // holds keys 16*(c/2) + 4*(c%2) + {0..3, 8..11}.
       uint8_t* vw = smem + stage * STAGE + K_BYTES;
       for (int p = tid; p < DK * 8; p += NT) {
         const int row = p / 8, c = p % 8;
@@ -202,7 +204,8 @@ attn_f16_kernel(AttnF16Args a) {
         uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int key = k0 + c * 8 + 2 * e;
+          // elements 2e and 2e+1 of the chunk
+          const int key = k0 + 16 * (c >> 1) + 4 * (c & 1) + (2 * e & 3) + 8 * (e >> 1);
           if (key >= a.T_k) w[e] = 0u;
           else if (key + 1 >= a.T_k) w[e] &= 0xffffu;
         }
@@ -300,17 +303,15 @@ attn_f16_kernel(AttnF16Args a) {
       l_run[qi] += rs;
 
       // P^T fragment c covers keys c*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}; V^T
-      // supplies the same keys for its row d: 8-byte halves of chunks 2c and
-      // 2c+1.
+      // row d supplies the same keys as its chunk 2c + lh.
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int row = dt * 32 + lq;
-        const uint8_t* vrow = Vs + row * 128 + lh * 8;
+        const uint8_t* vrow = Vs + row * 128;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + swz<8>(row, 2 * c) * 16);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + swz<8>(row, 2 * c + 1) * 16);
-          o[qi][dt] = mfma32x32x16<F16>(u32x4{lo.x, lo.y, hi.x, hi.y}, pf[c], o[qi][dt]);
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + swz<8>(row, 2 * c + lh) * 16);
+          o[qi][dt] = mfma32x32x16<F16>(vf, pf[c], o[qi][dt]);
         }
       }
     }

@@ -44,6 +44,22 @@ __device__ __forceinline__ f32x16_t mfma32x32x16<F16>(const u32x4& a, const u32x
                                                 __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
 }
 
+// Asynchronous global -> LDS copy (global_load_lds): every active lane copies
+// BYTES bytes from its own global address; lane L's bytes land at
+// lds_base + BYTES * L. lds_base must be the same for the whole wave. Counted
+// by vmcnt like any vector load. (Kept out of templates: calling the builtin
+// directly in a kernel template left the template's host stub undefined.)
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(
+      (const __attribute__((address_space(1))) void*)gsrc,
+      (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(
+      (const __attribute__((address_space(1))) void*)gsrc,
+      (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
 __device__ __forceinline__ f32x4_t mfma16x16x4f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

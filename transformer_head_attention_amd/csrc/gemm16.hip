@@ -18,22 +18,27 @@
 
 namespace mha {
 
-namespace {
+// Kernel templates are instantiated directly in the non-template launch
+// functions below (instantiating them from inside another template left their
+// host stubs undefined).
+namespace gemm_impl {
 
-constexpr int BK = 64;          // K slice per stage (16-bit elements)
-constexpr int LDS_STRIDE = BK + 8;   // padded LDS row, in 16-bit elements
+constexpr int BK = 64;   // K slice per stage (16-bit elements): 128-byte LDS rows
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int NS_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NS = NS_;
   static constexpr int WAVES_N = BN / WN;
   static constexpr int NWAVES = (BM / WM) * WAVES_N;
   static constexpr int NT = NWAVES * 64;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int A_PER_T = BM * BK / 8 / NT;   // 16-byte chunks per thread
-  static constexpr int B_PER_T = BN * BK / 8 / NT;
-  static constexpr int STAGE = (BM + BN) * LDS_STRIDE;
-  static_assert(BM * BK / 8 % NT == 0 && BN * BK / 8 % NT == 0, "tile / thread mismatch");
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LPT = A_BYTES / 16 / NT;   // DMA loads per thread per K slice
+  static constexpr int B_LPT = B_BYTES / 16 / NT;
+  static constexpr int LPT = A_LPT + B_LPT;
+  static_assert(A_BYTES % (16 * NT) == 0 && B_BYTES % (16 * NT) == 0, "tile / thread mismatch");
+  static_assert(NS >= 2 && NS <= 3, "pipeline depth");
 };
 
 // Map a linear workgroup id so that consecutive logical tiles land on the same
@@ -44,48 +49,64 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
   return (L % 8) * per + L / 8;
 }
 
-template <typename C, typename Tag, typename Epi>
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16-byte chunk c of LDS row `row` (8 chunks per 128-byte row) is stored at
+// chunk c ^ ((row >> 1) & 7): the 32 rows read by one MFMA operand load then
+// spread over all banks.
+__device__ __forceinline__ int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+// TRANS computes each 32 x 32 tile as (B^T A^T)^T: the MFMA result then holds,
+// per lane, one row m and four consecutive columns n (instead of one column
+// and four consecutive rows).
+template <typename C, typename Tag, bool TRANS, typename Epi>
 __global__ void __launch_bounds__(C::NT)
 gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, int M, int N,
               int K, Epi epi) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NS * C::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
-  // Tile order: column tiles of one row band are consecutive, and a group of
-  // row bands shares an XCD so that its A rows and all of B stay in that L2.
+  // Tile order: each XCD takes a contiguous range of logical tiles, walked in
+  // groups of GM row bands so that the concurrently resident workgroups of
+  // an XCD share A rows and B columns in its L2.
+#ifndef MHA_GEMM_GM
+#define MHA_GEMM_GM 4
+#endif
+  constexpr int GM = MHA_GEMM_GM;
   const int ntn = (N + C::BN - 1) / C::BN, ntm = (M + C::BM - 1) / C::BM;
   const int logical = xcd_remap(blockIdx.x, ntn * ntm);
-  const int bm = logical / ntn, bn = logical % ntn;
+  const int group = logical / (GM * ntn);
+  const int gm0 = group * GM, gsz = min(GM, ntm - gm0);
+  const int in_group = logical - group * GM * ntn;
+  const int bm = gm0 + in_group % gsz, bn = in_group / gsz;
   const int m0 = bm * C::BM, n0 = bn * C::BN;
 
-  u32x4 ra[C::A_PER_T], rb[C::B_PER_T];
-  auto gload = [&](int k0) __attribute__((always_inline)) {
+  // DMA of K slice kt into stage `stage`: lane chunk p of a wave-wide load
+  // lands at byte 16*p of the wave's 1 KiB window and fetches the global
+  // chunk the swizzled layout places there. Rows past M or N are clamped
+  // (their results are never stored).
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    uint8_t* as = smem + stage * C::STAGE;
+    uint8_t* bs = as + C::A_BYTES;
+    const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-      const int c = tid + i * C::NT, row = c / (BK / 8), col = (c % (BK / 8)) * 8;
+    for (int i = 0; i < C::A_LPT; ++i) {
+      const int p = i * C::NT + tid, row = p / 8, c = swz8(row, p % 8);
       const int m = min(m0 + row, M - 1);
-      ra[i] = *reinterpret_cast<const u32x4*>(A + (size_t)m * K + k0 + col);
+      lds_dma16(A + (size_t)m * K + k0 + c * 8,
+                as + (i * C::NT + wave * 64) * 16);
     }
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-      const int c = tid + i * C::NT, row = c / (BK / 8), col = (c % (BK / 8)) * 8;
+    for (int i = 0; i < C::B_LPT; ++i) {
+      const int p = i * C::NT + tid, row = p / 8, c = swz8(row, p % 8);
       const int n = min(n0 + row, N - 1);
-      rb[i] = *reinterpret_cast<const u32x4*>(Bt + (size_t)n * K + k0 + col);
-    }
-  };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* As = smem + buf * C::STAGE;
-    uint16_t* Bs = As + C::BM * LDS_STRIDE;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-      const int c = tid + i * C::NT, row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-      *reinterpret_cast<u32x4*>(As + row * LDS_STRIDE + col) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-      const int c = tid + i * C::NT, row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Bs + row * LDS_STRIDE + col) = rb[i];
+      lds_dma16(Bt + (size_t)n * K + k0 + c * 8,
+                bs + (i * C::NT + wave * 64) * 16);
     }
   };
 
@@ -98,97 +119,199 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int arow = wm * C::WM + (lane & 31), brow = wn * C::WN + (lane & 31);
-  const int kofs = (lane >> 5) * 8;
+#pragma unroll
+  for (int t = 0; t < C::NS - 1; ++t)
+    if (t < nk) issue(t, t);
+
+  const int arow0 = wm * C::WM + (lane & 31), brow0 = wn * C::WN + (lane & 31);
+  const int lh = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const uint16_t* As = smem + (kt & 1) * C::STAGE;
-    const uint16_t* Bs = As + C::BM * LDS_STRIDE;
+    if (C::NS == 3 && kt + 1 < nk) wait_vmcnt<C::LPT>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();   // slice kt has landed; the stage read last is free
+    if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
+    const uint8_t* as = smem + (kt % C::NS) * C::STAGE;
+    const uint8_t* bs = as + C::A_BYTES;
+    // Operand fragments are double-buffered in registers: the LDS reads of
+    // k-step ks+1 are issued before the MFMAs of k-step ks, so their latency
+    // hides behind 16 MFMAs of this wave.
+    u32x4 a[2][C::TM], b[2][C::TN];
+    auto frags = [&](int ks, u32x4 (&fa)[C::TM], u32x4 (&fb)[C::TN]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const int row = arow0 + i * 32;
+        fa[i] = *reinterpret_cast<const u32x4*>(as + (row * 8 + swz8(row, 2 * ks + lh)) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int row = brow0 + j * 32;
+        fb[j] = *reinterpret_cast<const u32x4*>(bs + (row * 8 + swz8(row, 2 * ks + lh)) * 16);
+      }
+    };
+    frags(0, a[0], b[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 a[C::TM], b[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(As + (arow + i * 32) * LDS_STRIDE + ks * 16 + kofs);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(Bs + (brow + j * 32) * LDS_STRIDE + ks * 16 + kofs);
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) frags(ks + 1, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32x32x16<Tag>(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < C::TN; ++j)
+          acc[i][j] = TRANS ? mfma32x32x16<Tag>(b[cur][j], a[cur][i], acc[i][j])
+                            : mfma32x32x16<Tag>(a[cur][i], b[cur][j], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore((kt + 1) & 1);
-    __syncthreads();
+    // Issue order for the scheduler (0x100 = LDS read, 0x008 = MFMA): the
+    // fragments of k-step 0, then in each k-step the next step's reads go
+    // out one per MFMA over the first half of its MFMAs, so the second half
+    // covers their latency before the next step's first MFMA waits on them.
+    static_assert(BK / 16 == 4 && C::TM + C::TN <= C::TM * C::TN, "schedule shape");
+    __builtin_amdgcn_sched_group_barrier(0x100, C::TM + C::TN, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+#pragma unroll
+      for (int r = 0; r < C::TM + C::TN; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN - (C::TM + C::TN), 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN, 0);
   }
   epi.template apply<C::TM, C::TN>(acc, m0 + wm * C::WM, n0 + wn * C::WN, lane, M, N);
 }
 
-// Head-split epilogue of the QKV projection.
-struct QkvEpi {
+// Head-split epilogues of the QKV projection. Column n of [Q|K|V] is head
+// (n mod D) / d_k, channel (n mod D) mod d_k; row m is batch m / T, position
+// m mod T.
+//
+// Q and K columns (transposed tiles): a lane holds row m and channels
+// n..n+3, written as one 8-byte store into (B, h, T, d_k); Q is scaled by
+// q_scale. Rows t < early_rows are also written in fp32 (16-byte stores).
+struct QkEpi {
   QkvEpilogue e;
   template <int TM, int TN>
   __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
                                         int M, int N) const {
-    const int D = e.D, d_k = e.d_k;
+    const int D = e.D, d_k = e.d_k, T = e.T, lq = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mbase + i * 32 + lq;
+      if (m >= M) continue;
+      const int b = m / T, t = m - b * T;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = nbase + j * 32 + 8 * rg + 4 * lh;   // four columns n..n+3
+          if (n >= N) continue;
+          const int ng = e.n_base + n;
+          const int which = ng / D, hc = ng - which * D, head = hc / d_k, c = hc - head * d_k;
+          float v[4];
+          if (e.bias) {
+            const u32x2 bb = *reinterpret_cast<const u32x2*>(e.bias + ng);
+            v[0] = acc[i][j][rg * 4 + 0] + __uint_as_float(bb.x << 16);
+            v[1] = acc[i][j][rg * 4 + 1] + __uint_as_float(bb.x & 0xffff0000u);
+            v[2] = acc[i][j][rg * 4 + 2] + __uint_as_float(bb.y << 16);
+            v[3] = acc[i][j][rg * 4 + 3] + __uint_as_float(bb.y & 0xffff0000u);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[i][j][rg * 4 + r];
+          }
+          if (e.early && t < e.early_rows)
+            *reinterpret_cast<f32x4_t*>(e.early + ((size_t)b * e.early_rows + t) * (3 * D) + ng) =
+                f32x4_t{v[0], v[1], v[2], v[3]};
+          const float sc = which == 0 ? e.q_scale : 1.0f;
+          const int tpad = which == 0 ? e.Tpad_q : e.Tpad_kv;
+          uint16_t* dst = (which == 0 ? e.q : e.k) +
+                          (((size_t)b * e.h + head) * tpad + t) * d_k + c;
+          *reinterpret_cast<u32x2*>(dst) =
+              u32x2{pack_f16x2(v[0] * sc, v[1] * sc), pack_f16x2(v[2] * sc, v[3] * sc)};
+        }
+      }
+    }
+  }
+};
+
+// Position of key t in a V^T row: bits 2 and 3 of t swapped, so each 16-key
+// group is stored as keys {0-3, 8-11, 4-7, 12-15}. One 16-byte chunk then
+// holds exactly the 8 keys one lane half of the P.V MFMA consumes.
+__device__ __forceinline__ int vt_pos(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
+// V columns (normal tiles): a lane holds column n and rows m..m+3, i.e. four
+// consecutive positions of one V^T row, written as one 8-byte store (a group
+// of four stays contiguous under vt_pos).
+struct VEpi {
+  QkvEpilogue e;
+  template <int TM, int TN>
+  __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
+                                        int M, int N) const {
+    const int D = e.D, d_k = e.d_k, T = e.T, lh = lane >> 5;
+    // Usually the wave's TM*32 rows lie in one batch element: one division.
+    const int bw = mbase / T, tw = mbase - bw * T;
+    const bool one_batch = (T & 3) == 0 && tw + TM * 32 <= T && mbase + TM * 32 <= M;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int n = nbase + j * 32 + (lane & 31);
       if (n >= N) continue;
       const int ng = e.n_base + n;
-      const int which = ng / D, hc = ng - which * D;
-      const int head = hc / d_k, c = hc - head * d_k;
+      const int hc = ng - 2 * D, head = hc / d_k, c = hc - head * d_k;
+      if (one_batch) {
+        uint16_t* row = e.vt + (((size_t)bw * e.h + head) * d_k + c) * e.Tpad_kv;
+        const float bias = load_bias_bf16(e.bias, ng);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int t0 = tw + i * 32 + 8 * rg + 4 * lh;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[i][j][rg * 4 + r] + bias;
+            if (e.early && t0 < e.early_rows) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (t0 + r < e.early_rows)
+                  e.early[((size_t)bw * e.early_rows + t0 + r) * (3 * D) + ng] = v[r];
+            }
+            *reinterpret_cast<u32x2*>(row + vt_pos(t0)) =
+                u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+          }
+        continue;
+      }
       const float bias = load_bias_bf16(e.bias, ng);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const int mf = mbase + i * 32 + 8 * rg + 4 * (lane >> 5);
+          const int mf = mbase + i * 32 + 8 * rg + 4 * lh;
+          if (mf >= M) continue;
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = acc[i][j][rg * 4 + r] + bias;
-          const int b0 = mf / e.T, t0 = mf - b0 * e.T;
-          if (e.early && (t0 < e.early_rows || t0 + 4 > e.T)) {
+          const int b0 = mf / T, t0 = mf - b0 * T;
+          if ((t0 & 3) == 0 && t0 + 3 < T && mf + 3 < M) {
+            if (e.early && t0 < e.early_rows) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int m = mf + r;
-              if (m >= M) break;
-              const int b = m / e.T, t = m - b * e.T;
-              if (t < e.early_rows)
-                e.early[((size_t)b * e.early_rows + t) * (3 * D) + ng] = v[r];
+              for (int r = 0; r < 4; ++r)
+                if (t0 + r < e.early_rows)
+                  e.early[((size_t)b0 * e.early_rows + t0 + r) * (3 * D) + ng] = v[r];
             }
+            uint16_t* row = e.vt + (((size_t)b0 * e.h + head) * d_k + c) * e.Tpad_kv;
+            *reinterpret_cast<u32x2*>(row + vt_pos(t0)) =
+                u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+            continue;
           }
-          if (which == 2) {
-            // V^T: four consecutive t of one column -> one 8-byte store when aligned.
-            if ((e.T & 3) == 0 && mf + 3 < M) {
-              uint16_t* dst = e.vt + (((size_t)b0 * e.h + head) * d_k + c) * e.Tpad_kv + t0;
-              u32x2 pk;
-              pk.x = pack_f16x2(v[0], v[1]);
-              pk.y = pack_f16x2(v[2], v[3]);
-              *reinterpret_cast<u32x2*>(dst) = pk;
-            } else {
+          // rows that cross a batch boundary, are unaligned, or pass the end of M
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int m = mf + r;
-                if (m >= M) break;
-                const int b = m / e.T, t = m - b * e.T;
-                e.vt[(((size_t)b * e.h + head) * d_k + c) * e.Tpad_kv + t] = float_to_f16_bits(v[r]);
-              }
-            }
-          } else {
-            uint16_t* base = which == 0 ? e.q : e.k;
-            const int tpad = which == 0 ? e.Tpad_q : e.Tpad_kv;
-            const float sc = which == 0 ? e.q_scale : 1.0f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int m = mf + r;
-              if (m >= M) break;
-              const int b = m / e.T, t = m - b * e.T;
-              base[(((size_t)b * e.h + head) * tpad + t) * d_k + c] = float_to_f16_bits(v[r] * sc);
-            }
+          for (int r = 0; r < 4; ++r) {
+            const int m = mf + r;
+            if (m >= M) break;
+            const int b = m / T, t = m - b * T;
+            if (e.early && t < e.early_rows)
+              e.early[((size_t)b * e.early_rows + t) * (3 * D) + ng] = v[r];
+            e.vt[(((size_t)b * e.h + head) * d_k + c) * e.Tpad_kv + vt_pos(t)] =
+                float_to_f16_bits(v[r]);
           }
         }
       }
@@ -272,19 +395,56 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
   }
 }
 
-using QkvCfg = Cfg<128, 128, 64, 64>;
-using OutCfg = Cfg<128, 128, 64, 64>;
+// Large problems: 256 x 256 tiles, four waves of 128 x 128 (accumulators in
+// AGPRs, one wave per SIMD). Problems with too few such tiles to fill the
+// 256 CUs use 128 x 128 tiles, four waves of 64 x 64.
+using BigCfg = Cfg<256, 256, 128, 128, 2>;
+using SmallCfg = Cfg<128, 128, 64, 64, 2>;
 
+int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
+#ifndef MHA_GEMM_BIG_MIN_TILES
+#define MHA_GEMM_BIG_MIN_TILES 384
+#endif
+bool use_big(int M, int N) { return tiles_of(M, N, 256, 256) >= MHA_GEMM_BIG_MIN_TILES; }
+
+}  // namespace gemm_impl
+
+using namespace gemm_impl;
+
+namespace {
+template <bool TRANS, typename Epi>
+hipError_t launch_qkv_part(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
+                           const Epi& epi, hipStream_t s) {
+  // The V epilogue holds too many live values next to 256 accumulators per
+  // lane: V columns always use the 128 x 128 tiles.
+  if (TRANS && use_big(M, N))
+    hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi>), dim3(tiles_of(M, N, 256, 256)),
+                       dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
+  else
+    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi>),
+                       dim3(tiles_of(M, N, 128, 128)), dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K,
+                       epi);
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
                            const QkvEpilogue& e, hipStream_t s) {
-  using C = QkvCfg;
-  const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
-  QkvEpi epi{e};
-  hipLaunchKernelGGL((gemm16_kernel<C, BF16, QkvEpi>), dim3(tiles), dim3(C::NT), 0, s, A, Bt, M,
-                     N, K, epi);
-  return hipGetLastError();
+  // Columns [n_base, n_base + N) of [Q|K|V]: the Q and K part runs with
+  // transposed tiles, the V part with normal tiles.
+  const int n_lo = e.n_base, n_hi = e.n_base + N, split = 2 * e.D;
+  if (n_lo < split) {
+    QkEpi epi{e};
+    const hipError_t err = launch_qkv_part<true>(A, M, K, Bt, min(n_hi, split) - n_lo, epi, s);
+    if (err != hipSuccess) return err;
+  }
+  if (n_hi > split) {
+    const int v_lo = max(n_lo, split);
+    VEpi epi{e};
+    epi.e.n_base = v_lo;
+    return launch_qkv_part<false>(A, M, K, Bt + (size_t)(v_lo - n_lo) * K, n_hi - v_lo, epi, s);
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
@@ -296,11 +456,13 @@ hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT,
 
 hipError_t launch_gemm_out(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
                            const uint16_t* bias, float* Y, hipStream_t s) {
-  using C = OutCfg;
-  const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
   OutEpi epi{bias, Y};
-  hipLaunchKernelGGL((gemm16_kernel<C, F16, OutEpi>), dim3(tiles), dim3(C::NT), 0, s, A, Bt, M, N,
-                     K, epi);
+  if (use_big(M, N))
+    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, false, OutEpi>), dim3(tiles_of(M, N, 256, 256)),
+                       dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
+  else
+    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, false, OutEpi>), dim3(tiles_of(M, N, 128, 128)),
+                       dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K, epi);
   return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ struct QkvEpilogue {
   const uint16_t* bias;  // (3D) bf16, or null
   uint16_t* q;           // (B, h, Tpad_q, d_k) fp16 -- columns [0, D)
   uint16_t* k;           // (B, h, Tpad_kv, d_k) fp16 -- columns [D, 2D)
-  uint16_t* vt;          // (B, h, d_k, Tpad_kv) fp16 -- columns [2D, 3D), transposed
+  uint16_t* vt;          // (B, h, d_k, Tpad_kv) fp16 -- columns [2D, 3D), transposed;
+                         // position t stored at vt_pos(t) (bits 2 and 3 swapped)
   float* early;          // (B, early_rows, 3D) fp32 copy of rows t < early_rows, or null
   int early_rows;
   float q_scale;         // multiplies the fp16 Q (the fp32 early copy is unscaled)
@@ -50,7 +51,7 @@ hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT,
 struct AttnF16Args {
   const uint16_t* q;   // (B, h, Tqp, d_k) fp16, pre-multiplied by log2(e)/sqrt(d_k)
   const uint16_t* k;   // (B, h, Tkp, d_k) fp16
-  const uint16_t* vt;  // (B, h, d_k, Tkp) fp16
+  const uint16_t* vt;  // (B, h, d_k, Tkp) fp16, positions permuted as the QKV epilogue stores them
   uint16_t* o;         // (B, T_q, D) fp16, head i at columns [i*d_k, (i+1)*d_k)
   const uint32_t* mbits;  // (B, mbits_ld, 2) ignore bitmask per 64-key tile, or null
   int mbits_ld;           // 64-key tiles per batch element (attn_mask_tiles(T_k))
