@@ -269,7 +269,7 @@ attn_f16_kernel(AttnF16Args a) {
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qi][kh][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pair32_max(mx);
       const bool first = !seen[qi] && mx != -INFINITY;
       const float shift = first ? mx : (mx > 8.0f ? mx : 0.0f);
       if (__ballot(shift != 0.0f)) {
@@ -320,7 +320,7 @@ attn_f16_kernel(AttnF16Args a) {
   // O = acc / l; head `head` occupies columns [head*DK, (head+1)*DK) of (B, T_q, D).
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
-    const float lt = l_run[qi] + __shfl_xor(l_run[qi], 32);
+    const float lt = pair32_sum(l_run[qi]);
     const float inv = 1.0f / lt;
     const int row = qw0 + qi * 32 + lq;
     if (row < a.T_q) {
@@ -344,7 +344,7 @@ attn_f16_kernel(AttnF16Args a) {
 #define MHA_ATTN_NQ64 1
 #endif
 #ifndef MHA_ATTN_NS64
-#define MHA_ATTN_NS64 4
+#define MHA_ATTN_NS64 3
 #endif
 #ifndef MHA_ATTN_NS128
 #define MHA_ATTN_NS128 3

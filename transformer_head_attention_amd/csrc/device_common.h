@@ -92,4 +92,18 @@ __device__ __forceinline__ float load_bias_bf16(const uint16_t* b, int i) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: a VALU
+// exchange of the two lane halves, no LDS round trip). Swapping v with itself
+// leaves each lane's own value in one result and its partner's in the other.
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace mha

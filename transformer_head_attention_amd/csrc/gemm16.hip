@@ -23,11 +23,12 @@ namespace mha {
 // host stubs undefined).
 namespace gemm_impl {
 
-constexpr int BK = 64;   // K slice per stage (16-bit elements): 128-byte LDS rows
-
-template <int BM_, int BN_, int WM_, int WN_, int NS_>
+// BM x BN output tile, WM x WN per wave, BK-deep K slices (32 or 64 16-bit
+// elements: 64- or 128-byte LDS rows), NS slices in flight.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NS = NS_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int CH = BK / 8;                 // 16-byte chunks per LDS row
   static constexpr int WAVES_N = BN / WN;
   static constexpr int NWAVES = (BM / WM) * WAVES_N;
   static constexpr int NT = NWAVES * 64;
@@ -38,7 +39,8 @@ struct Cfg {
   static constexpr int B_LPT = B_BYTES / 16 / NT;
   static constexpr int LPT = A_LPT + B_LPT;
   static_assert(A_BYTES % (16 * NT) == 0 && B_BYTES % (16 * NT) == 0, "tile / thread mismatch");
-  static_assert(NS >= 2 && NS <= 3, "pipeline depth");
+  static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+  static_assert(BK == 32 || BK == 64, "K slice");
 };
 
 // Map a linear workgroup id so that consecutive logical tiles land on the same
@@ -55,10 +57,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// 16-byte chunk c of LDS row `row` (8 chunks per 128-byte row) is stored at
-// chunk c ^ ((row >> 1) & 7): the 32 rows read by one MFMA operand load then
-// spread over all banks.
-__device__ __forceinline__ int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
+// 16-byte chunk c of LDS row `row` is stored at a row-dependent XOR of c, so
+// that the 16 rows one quarter-wave reads for an MFMA operand cover all 64
+// banks: 128-byte rows (8 chunks) pair up per 256-byte bank window, 64-byte
+// rows (4 chunks) group by four.
+template <int CH>
+__device__ __forceinline__ int swz(int row, int c) {
+  return CH == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
+}
 
 // TRANS computes each 32 x 32 tile as (B^T A^T)^T: the MFMA result then holds,
 // per lane, one row m and four consecutive columns n (instead of one column
@@ -68,7 +74,9 @@ __global__ void __launch_bounds__(C::NT)
 gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, int M, int N,
               int K, Epi epi) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NS * C::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index in a scalar register: the DMA LDS bases below stay scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   // Tile order: each XCD takes a contiguous range of logical tiles, walked in
@@ -93,17 +101,17 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     uint8_t* as = smem + stage * C::STAGE;
     uint8_t* bs = as + C::A_BYTES;
-    const int k0 = kt * BK;
+    const int k0 = kt * C::BK;
 #pragma unroll
     for (int i = 0; i < C::A_LPT; ++i) {
-      const int p = i * C::NT + tid, row = p / 8, c = swz8(row, p % 8);
+      const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
       const int m = min(m0 + row, M - 1);
       lds_dma16(A + (size_t)m * K + k0 + c * 8,
                 as + (i * C::NT + wave * 64) * 16);
     }
 #pragma unroll
     for (int i = 0; i < C::B_LPT; ++i) {
-      const int p = i * C::NT + tid, row = p / 8, c = swz8(row, p % 8);
+      const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
       const int n = min(n0 + row, N - 1);
       lds_dma16(Bt + (size_t)n * K + k0 + c * 8,
                 bs + (i * C::NT + wave * 64) * 16);
@@ -118,7 +126,7 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = K / BK;
+  const int nk = K / C::BK;
 #pragma unroll
   for (int t = 0; t < C::NS - 1; ++t)
     if (t < nk) issue(t, t);
@@ -126,10 +134,13 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   const int arow0 = wm * C::WM + (lane & 31), brow0 = wn * C::WN + (lane & 31);
   const int lh = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
-    if (C::NS == 3 && kt + 1 < nk) wait_vmcnt<C::LPT>();
+    // Slice kt is complete once at most the younger slices' loads are
+    // outstanding (up to NS-2 of them).
+    const int younger = min(C::NS - 2, nk - 1 - kt);
+    if (younger >= 2) wait_vmcnt<2 * C::LPT>();
+    else if (younger == 1) wait_vmcnt<C::LPT>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();   // slice kt has landed; the stage read last is free
-    if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
     const uint8_t* as = smem + (kt % C::NS) * C::STAGE;
     const uint8_t* bs = as + C::A_BYTES;
     // Operand fragments are double-buffered in registers: the LDS reads of
@@ -140,19 +151,19 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         const int row = arow0 + i * 32;
-        fa[i] = *reinterpret_cast<const u32x4*>(as + (row * 8 + swz8(row, 2 * ks + lh)) * 16);
+        fa[i] = *reinterpret_cast<const u32x4*>(as + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         const int row = brow0 + j * 32;
-        fb[j] = *reinterpret_cast<const u32x4*>(bs + (row * 8 + swz8(row, 2 * ks + lh)) * 16);
+        fb[j] = *reinterpret_cast<const u32x4*>(bs + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
       }
     };
     frags(0, a[0], b[0]);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < C::BK / 16; ++ks) {
       const int cur = ks & 1;
-      if (ks + 1 < BK / 16) frags(ks + 1, a[cur ^ 1], b[cur ^ 1]);
+      if (ks + 1 < C::BK / 16) frags(ks + 1, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -160,39 +171,131 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
           acc[i][j] = TRANS ? mfma32x32x16<Tag>(b[cur][j], a[cur][i], acc[i][j])
                             : mfma32x32x16<Tag>(a[cur][i], b[cur][j], acc[i][j]);
     }
-    // Issue order for the scheduler (0x100 = LDS read, 0x008 = MFMA): the
-    // fragments of k-step 0, then in each k-step the next step's reads go
-    // out one per MFMA over the first half of its MFMAs, so the second half
-    // covers their latency before the next step's first MFMA waits on them.
-    static_assert(BK / 16 == 4 && C::TM + C::TN <= C::TM * C::TN, "schedule shape");
-    __builtin_amdgcn_sched_group_barrier(0x100, C::TM + C::TN, 0);
+    // Slice kt+NS-1 goes into the stage read in the previous iteration. The
+    // load is issued every iteration (past the last slice it re-reads the
+    // last slice into a stage nobody reads again), which keeps it in the same
+    // basic block as the MFMAs so the two can interleave.
+    issue(min(kt + C::NS - 1, nk - 1), (kt + C::NS - 1) % C::NS);
+    // Issue order for the scheduler (0x100 = LDS read, 0x008 = MFMA,
+    // 0x020 = global load): the fragments of k-step 0; in each k-step but the
+    // last, the next step's reads go out one per MFMA over its first MFMAs so
+    // the rest cover their latency; in the last k-step the next slices'
+    // global->LDS loads go out between MFMAs.
+    constexpr int KS = C::BK / 16, NR = C::TM + C::TN, NMF = C::TM * C::TN;
+    constexpr int VPER = (C::LPT + NMF - 1) / NMF, NV = (C::LPT + VPER - 1) / VPER;
+    static_assert(NR <= NMF && NV <= NMF, "schedule shape");
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+    for (int ks = 0; ks < KS - 1; ++ks) {
 #pragma unroll
-      for (int r = 0; r < C::TM + C::TN; ++r) {
+      for (int r = 0; r < NR; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN - (C::TM + C::TN), 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF - NR, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN, 0);
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, VPER, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF - NV, 0);
   }
-  epi.template apply<C::TM, C::TN>(acc, m0 + wm * C::WM, n0 + wn * C::WN, lane, M, N);
+  wait_vmcnt<0>();   // no global->LDS copy may outlive the workgroup
+  // Every wave has finished reading the stages: each wave may now use its
+  // share of the LDS to stage its output tile.
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  static_assert(C::WM * C::WN * 2 <= C::NS * C::STAGE / C::NWAVES, "staging window");
+  epi.template apply<C::TM, C::TN>(acc, m0 + wm * C::WM, n0 + wn * C::WN, lane, M, N,
+                                   smem + wave * (C::NS * C::STAGE / C::NWAVES));
+}
+
+// Output staging: 16-byte chunk c of LDS row `row` (RB bytes per row) sits at
+// a row-dependent XOR of c so that the 8-byte writes of 32 lanes to 32
+// consecutive rows spread over the banks.
+template <int RB>
+__device__ __forceinline__ int stage_chunk(int row, int c) {
+  return RB == 128 ? (c ^ ((row >> 1) & 7)) : (c ^ (row & 15));
 }
 
 // Head-split epilogues of the QKV projection. Column n of [Q|K|V] is head
 // (n mod D) / d_k, channel (n mod D) mod d_k; row m is batch m / T, position
-// m mod T.
-//
+// m mod T. A wave's tile is staged in LDS and written back 16 bytes per lane,
+// so each store instruction covers whole contiguous lines; tiles that cross a
+// batch boundary or the matrix edge are stored directly from registers.
+
+// Position of key t in a V^T row: bits 2 and 3 of t swapped, so each 16-key
+// group is stored as keys {0-3, 8-11, 4-7, 12-15}. One 16-byte chunk then
+// holds exactly the 8 keys one lane half of the P.V MFMA consumes.
+__device__ __forceinline__ int vt_pos(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
 // Q and K columns (transposed tiles): a lane holds row m and channels
-// n..n+3, written as one 8-byte store into (B, h, T, d_k); Q is scaled by
-// q_scale. Rows t < early_rows are also written in fp32 (16-byte stores).
+// n..n+3. Q is scaled by q_scale; rows t < early_rows are also written in fp32.
 struct QkEpi {
   QkvEpilogue e;
+
+  __device__ __forceinline__ void bias4(int ng, const f32x16_t& a, int r0, float (&v)[4]) const {
+    if (e.bias) {
+      const u32x2 bb = *reinterpret_cast<const u32x2*>(e.bias + ng);
+      v[0] = a[r0 + 0] + __uint_as_float(bb.x << 16);
+      v[1] = a[r0 + 1] + __uint_as_float(bb.x & 0xffff0000u);
+      v[2] = a[r0 + 2] + __uint_as_float(bb.y << 16);
+      v[3] = a[r0 + 3] + __uint_as_float(bb.y & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = a[r0 + r];
+    }
+  }
+
   template <int TM, int TN>
   __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
-                                        int M, int N) const {
+                                        int M, int N, uint8_t* lds) const {
+    constexpr int WM = TM * 32, WN = TN * 32, RB = WN * 2, CPR = WN / 8;
     const int D = e.D, d_k = e.d_k, T = e.T, lq = lane & 31, lh = lane >> 5;
+    const int bw = mbase / T, tw = mbase - bw * T;
+    const bool staged = tw + WM <= T && mbase + WM <= M && nbase + WN <= N;
+    const bool early = e.early && tw < e.early_rows;
+    if (staged) {
+      // The wave's WN columns lie in one of Q or K (WN divides D).
+      const int ng0 = e.n_base + nbase, which = ng0 / D, hc0 = ng0 - which * D;
+      const float sc = which == 0 ? e.q_scale : 1.0f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = i * 32 + lq;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int c = j * 32 + 8 * rg + 4 * lh;
+            float v[4];
+            bias4(ng0 + c, acc[i][j], rg * 4, v);
+            if (early && tw + r < e.early_rows)
+              *reinterpret_cast<f32x4_t*>(e.early + ((size_t)bw * e.early_rows + tw + r) * (3 * D) +
+                                          ng0 + c) = f32x4_t{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<u32x2*>(lds + r * RB + stage_chunk<RB>(r, c >> 3) * 16 + lh * 8) =
+                u32x2{pack_f16x2(v[0] * sc, v[1] * sc), pack_f16x2(v[2] * sc, v[3] * sc)};
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+      // Write-back: chunk runs of one head are contiguous in (B, h, T, d_k).
+      const int hseg = min(WN, d_k), lg_cph = hseg == 128 ? 4 : 3;   // chunks per head segment
+      const int tpad = which == 0 ? e.Tpad_q : e.Tpad_kv;
+      uint16_t* base = (which == 0 ? e.q : e.k) + (size_t)bw * e.h * tpad * d_k;
+#pragma unroll 4
+      for (int k = 0; k < WM * CPR / 64; ++k) {
+        const int idx = k * 64 + lane;
+        const int cb = idx >> (lg_cph + __builtin_ctz(WM)), rem = idx & ((WM << lg_cph) - 1);
+        const int r = rem >> lg_cph, c8 = (cb << lg_cph) + (rem & ((1 << lg_cph) - 1));
+        const u32x4 val = *reinterpret_cast<const u32x4*>(lds + r * RB + stage_chunk<RB>(r, c8) * 16);
+        const int col = hc0 + c8 * 8, head = col / d_k, ch = col - head * d_k;
+        *reinterpret_cast<u32x4*>(base + ((size_t)head * tpad + tw + r) * d_k + ch) = val;
+      }
+      return;
+    }
+    // Direct path: 8-byte stores of four channels.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = mbase + i * 32 + lq;
@@ -207,16 +310,7 @@ struct QkEpi {
           const int ng = e.n_base + n;
           const int which = ng / D, hc = ng - which * D, head = hc / d_k, c = hc - head * d_k;
           float v[4];
-          if (e.bias) {
-            const u32x2 bb = *reinterpret_cast<const u32x2*>(e.bias + ng);
-            v[0] = acc[i][j][rg * 4 + 0] + __uint_as_float(bb.x << 16);
-            v[1] = acc[i][j][rg * 4 + 1] + __uint_as_float(bb.x & 0xffff0000u);
-            v[2] = acc[i][j][rg * 4 + 2] + __uint_as_float(bb.y << 16);
-            v[3] = acc[i][j][rg * 4 + 3] + __uint_as_float(bb.y & 0xffff0000u);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = acc[i][j][rg * 4 + r];
-          }
+          bias4(ng, acc[i][j], rg * 4, v);
           if (e.early && t < e.early_rows)
             *reinterpret_cast<f32x4_t*>(e.early + ((size_t)b * e.early_rows + t) * (3 * D) + ng) =
                 f32x4_t{v[0], v[1], v[2], v[3]};
@@ -232,53 +326,65 @@ struct QkEpi {
   }
 };
 
-// Position of key t in a V^T row: bits 2 and 3 of t swapped, so each 16-key
-// group is stored as keys {0-3, 8-11, 4-7, 12-15}. One 16-byte chunk then
-// holds exactly the 8 keys one lane half of the P.V MFMA consumes.
-__device__ __forceinline__ int vt_pos(int t) {
-  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
-}
-
 // V columns (normal tiles): a lane holds column n and rows m..m+3, i.e. four
-// consecutive positions of one V^T row, written as one 8-byte store (a group
-// of four stays contiguous under vt_pos).
+// consecutive positions of one V^T row.
 struct VEpi {
   QkvEpilogue e;
   template <int TM, int TN>
   __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
-                                        int M, int N) const {
-    const int D = e.D, d_k = e.d_k, T = e.T, lh = lane >> 5;
-    // Usually the wave's TM*32 rows lie in one batch element: one division.
+                                        int M, int N, uint8_t* lds) const {
+    constexpr int WM = TM * 32, WN = TN * 32, RB = WM * 2, CPR = WM / 8;
+    const int D = e.D, d_k = e.d_k, T = e.T, lq = lane & 31, lh = lane >> 5;
     const int bw = mbase / T, tw = mbase - bw * T;
-    const bool one_batch = (T & 3) == 0 && tw + TM * 32 <= T && mbase + TM * 32 <= M;
+    // One batch element, a full tile, and a start on a 16-position group so
+    // the position permutation stays inside the tile.
+    const bool staged = (tw & 15) == 0 && tw + WM <= T && mbase + WM <= M && nbase + WN <= N;
+    if (staged) {
+      const int hc0 = e.n_base + nbase - 2 * D;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = nbase + j * 32 + (lane & 31);
-      if (n >= N) continue;
-      const int ng = e.n_base + n;
-      const int hc = ng - 2 * D, head = hc / d_k, c = hc - head * d_k;
-      if (one_batch) {
-        uint16_t* row = e.vt + (((size_t)bw * e.h + head) * d_k + c) * e.Tpad_kv;
+      for (int j = 0; j < TN; ++j) {
+        const int c = j * 32 + lq;
+        const int ng = e.n_base + nbase + c;
         const float bias = load_bias_bf16(e.bias, ng);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const int t0 = tw + i * 32 + 8 * rg + 4 * lh;
+            const int r0 = i * 32 + 8 * rg + 4 * lh;
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[i][j][rg * 4 + r] + bias;
-            if (e.early && t0 < e.early_rows) {
+            if (e.early && tw + r0 < e.early_rows) {
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (t0 + r < e.early_rows)
-                  e.early[((size_t)bw * e.early_rows + t0 + r) * (3 * D) + ng] = v[r];
+                if (tw + r0 + r < e.early_rows)
+                  e.early[((size_t)bw * e.early_rows + tw + r0 + r) * (3 * D) + ng] = v[r];
             }
-            *reinterpret_cast<u32x2*>(row + vt_pos(t0)) =
+            const int pos = vt_pos(r0);
+            *reinterpret_cast<u32x2*>(lds + c * RB + stage_chunk<RB>(c, pos >> 3) * 16 +
+                                      (pos & 7) * 2) =
                 u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
           }
-        continue;
       }
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+      // Write-back: each V^T row segment of WM positions is contiguous.
+#pragma unroll 4
+      for (int k = 0; k < WN * CPR / 64; ++k) {
+        const int idx = k * 64 + lane;
+        const int c = idx / CPR, p8 = idx - c * CPR;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(lds + c * RB + stage_chunk<RB>(c, p8) * 16);
+        const int col = hc0 + c, head = col / d_k, ch = col - head * d_k;
+        *reinterpret_cast<u32x4*>(e.vt + (((size_t)bw * e.h + head) * d_k + ch) * e.Tpad_kv + tw +
+                                  p8 * 8) = val;
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = nbase + j * 32 + lq;
+      if (n >= N) continue;
+      const int ng = e.n_base + n;
+      const int hc = ng - 2 * D, head = hc / d_k, c = hc - head * d_k;
       const float bias = load_bias_bf16(e.bias, ng);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -289,20 +395,6 @@ struct VEpi {
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = acc[i][j][rg * 4 + r] + bias;
-          const int b0 = mf / T, t0 = mf - b0 * T;
-          if ((t0 & 3) == 0 && t0 + 3 < T && mf + 3 < M) {
-            if (e.early && t0 < e.early_rows) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (t0 + r < e.early_rows)
-                  e.early[((size_t)b0 * e.early_rows + t0 + r) * (3 * D) + ng] = v[r];
-            }
-            uint16_t* row = e.vt + (((size_t)b0 * e.h + head) * d_k + c) * e.Tpad_kv;
-            *reinterpret_cast<u32x2*>(row + vt_pos(t0)) =
-                u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
-            continue;
-          }
-          // rows that cross a batch boundary, are unaligned, or pass the end of M
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int m = mf + r;
@@ -325,7 +417,7 @@ struct OutEpi {
   float* Y;
   template <int TM, int TN>
   __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
-                                        int M, int N) const {
+                                        int M, int N, uint8_t* /*lds*/) const {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int n = nbase + j * 32 + (lane & 31);
@@ -398,8 +490,20 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
 // Large problems: 256 x 256 tiles, four waves of 128 x 128 (accumulators in
 // AGPRs, one wave per SIMD). Problems with too few such tiles to fill the
 // 256 CUs use 128 x 128 tiles, four waves of 64 x 64.
-using BigCfg = Cfg<256, 256, 128, 128, 2>;
-using SmallCfg = Cfg<128, 128, 64, 64, 2>;
+#ifndef MHA_BIG_BK
+#define MHA_BIG_BK 32
+#endif
+#ifndef MHA_BIG_NS
+#define MHA_BIG_NS 4
+#endif
+#ifndef MHA_SMALL_BK
+#define MHA_SMALL_BK 32
+#endif
+#ifndef MHA_SMALL_NS
+#define MHA_SMALL_NS 4
+#endif
+using BigCfg = Cfg<256, 256, 128, 128, MHA_BIG_BK, MHA_BIG_NS>;
+using SmallCfg = Cfg<128, 128, 64, 64, MHA_SMALL_BK, MHA_SMALL_NS>;
 
 int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 #ifndef MHA_GEMM_BIG_MIN_TILES
@@ -417,13 +521,17 @@ hipError_t launch_qkv_part(const uint16_t* A, int M, int K, const uint16_t* Bt, 
                            const Epi& epi, hipStream_t s) {
   // The V epilogue holds too many live values next to 256 accumulators per
   // lane: V columns always use the 128 x 128 tiles.
-  if (TRANS && use_big(M, N))
-    hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi>), dim3(tiles_of(M, N, 256, 256)),
-                       dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
-  else
-    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi>),
-                       dim3(tiles_of(M, N, 128, 128)), dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K,
-                       epi);
+  bool big = false;
+  if constexpr (TRANS) big = use_big(M, N);
+  if constexpr (TRANS) {
+    if (big) {
+      hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi>), dim3(tiles_of(M, N, 256, 256)),
+                         dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi>), dim3(tiles_of(M, N, 128, 128)),
+                     dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K, epi);
   return hipGetLastError();
 }
 }  // namespace

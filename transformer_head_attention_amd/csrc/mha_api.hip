@@ -28,7 +28,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/mha.h"
+#include "mha.h"   // include/ (on the include path)
 #include "kernels.h"
 
 struct mha_handle {
