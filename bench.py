@@ -15,7 +15,7 @@ Beside the headline rate the line carries:
                 the committed rocprofv3 counter summary, or null when that
                 summary was taken on a different kernel source.
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of
-                the same workload (one batch element).
+                the same workload (whole batch elements, about 10 s of work).
 """
 
 from __future__ import annotations
@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 METRIC = "MHA fwd TFLOP/s + % bf16 MFMA peak, D=1024 h=16 T=4096 causal, 1 GPU"
 PEAK_MFMA_16BIT_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "attention": ["transformer_head_attention_amd/csrc/attn16.hip",
                   "transformer_head_attention_amd/csrc/device_common.h"],
@@ -62,13 +62,14 @@ def stage_flops(w, stage: str) -> float:
     return 0.0
 
 
-def read_traffic(stage: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(stage: str, workload: str):
+    """HBM bytes per launch from the committed counter summary of this stage's
+    kernel on this workload, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"{stage}_hbm_{workload}.txt")
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.lstrip().startswith("#"):
                 k, v = line.split(":", 1)
@@ -181,7 +182,7 @@ def main() -> int:
     dom = max(("qkv_proj", "attention", "out_proj"), key=lambda s: stages[s])
     dom_ms = stages[dom]
     achieved = stage_flops(w, dom) / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
-    traffic = read_traffic(dom) if dom in KERNEL_SOURCES else None
+    traffic = read_traffic(dom, name) if dom in KERNEL_SOURCES else None
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
