@@ -13,6 +13,8 @@
 // N x K). Tiles are staged through LDS, double-buffered with a register
 // prefetch of the next K slice; each wave owns a WM x WN sub-tile computed
 // with v_mfma_f32_32x32x16.
+#include <utility>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -39,7 +41,7 @@ struct Cfg {
   static constexpr int B_LPT = B_BYTES / 16 / NT;
   static constexpr int LPT = A_LPT + B_LPT;
   static_assert(A_BYTES % (16 * NT) == 0 && B_BYTES % (16 * NT) == 0, "tile / thread mismatch");
-  static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+  static_assert(NS >= 2 && NS <= 5, "pipeline depth");
   static_assert(BK == 32 || BK == 64, "K slice");
 };
 
@@ -64,6 +66,34 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int CH>
 __device__ __forceinline__ int swz(int row, int c) {
   return CH == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
+}
+
+// Scheduling hints for one run of MFMAs (0x008 = MFMA, 0x100 = LDS read,
+// 0x020 = global load): SLOTS slots of one MFMA each, the NR LDS reads spread
+// over the first slots, then the NV global loads over the slots after them.
+constexpr int clamp_count(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
+
+template <int D, int V>
+__device__ __forceinline__ void sched_slot() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+  if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+}
+
+template <int SLOTS, int NR, int NV, int... S>
+__device__ __forceinline__ void sched_run(std::integer_sequence<int, S...>) {
+  constexpr int DPER = (NR + SLOTS - 1) / SLOTS;
+  constexpr int ND = DPER ? (NR + DPER - 1) / DPER : 0;
+  constexpr int VSL = SLOTS - ND > 0 ? SLOTS - ND : SLOTS;   // slots that take loads
+  constexpr int V0 = SLOTS - ND > 0 ? ND : 0;                 // first of them
+  constexpr int VPER = (NV + VSL - 1) / VSL;
+  (sched_slot<clamp_count(NR - S * DPER, DPER),
+              S < V0 ? 0 : clamp_count(NV - (S - V0) * VPER, VPER)>(), ...);
+}
+
+template <int SLOTS, int NR, int NV>
+__device__ __forceinline__ void sched_run() {
+  sched_run<SLOTS, NR, NV>(std::make_integer_sequence<int, SLOTS>{});
 }
 
 // TRANS computes each 32 x 32 tile as (B^T A^T)^T: the MFMA result then holds,
@@ -127,80 +157,90 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = K / C::BK;
-#pragma unroll
-  for (int t = 0; t < C::NS - 1; ++t)
-    if (t < nk) issue(t, t);
-
   const int arow0 = wm * C::WM + (lane & 31), brow0 = wn * C::WN + (lane & 31);
   const int lh = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    // Slice kt is complete once at most the younger slices' loads are
-    // outstanding (up to NS-2 of them).
-    const int younger = min(C::NS - 2, nk - 1 - kt);
-    if (younger >= 2) wait_vmcnt<2 * C::LPT>();
-    else if (younger == 1) wait_vmcnt<C::LPT>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();   // slice kt has landed; the stage read last is free
-    const uint8_t* as = smem + (kt % C::NS) * C::STAGE;
+  // Operand fragments of one 16-deep k-step, read from a stage.
+  auto frags = [&](const uint8_t* as, int ks, u32x4 (&fa)[C::TM], u32x4 (&fb)[C::TN])
+      __attribute__((always_inline)) {
     const uint8_t* bs = as + C::A_BYTES;
-    // Operand fragments are double-buffered in registers: the LDS reads of
-    // k-step ks+1 are issued before the MFMAs of k-step ks, so their latency
-    // hides behind 16 MFMAs of this wave.
-    u32x4 a[2][C::TM], b[2][C::TN];
-    auto frags = [&](int ks, u32x4 (&fa)[C::TM], u32x4 (&fb)[C::TN]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        const int row = arow0 + i * 32;
-        fa[i] = *reinterpret_cast<const u32x4*>(as + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
-      }
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int row = brow0 + j * 32;
-        fb[j] = *reinterpret_cast<const u32x4*>(bs + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
-      }
-    };
-    frags(0, a[0], b[0]);
-#pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < C::BK / 16) frags(ks + 1, a[cur ^ 1], b[cur ^ 1]);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          acc[i][j] = TRANS ? mfma32x32x16<Tag>(b[cur][j], a[cur][i], acc[i][j])
-                            : mfma32x32x16<Tag>(a[cur][i], b[cur][j], acc[i][j]);
+    for (int i = 0; i < C::TM; ++i) {
+      const int row = arow0 + i * 32;
+      fa[i] = *reinterpret_cast<const u32x4*>(as + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
     }
-    // Slice kt+NS-1 goes into the stage read in the previous iteration. The
-    // load is issued every iteration (past the last slice it re-reads the
-    // last slice into a stage nobody reads again), which keeps it in the same
-    // basic block as the MFMAs so the two can interleave.
-    issue(min(kt + C::NS - 1, nk - 1), (kt + C::NS - 1) % C::NS);
-    // Issue order for the scheduler (0x100 = LDS read, 0x008 = MFMA,
-    // 0x020 = global load): the fragments of k-step 0; in each k-step but the
-    // last, the next step's reads go out one per MFMA over its first MFMAs so
-    // the rest cover their latency; in the last k-step the next slices'
-    // global->LDS loads go out between MFMAs.
-    constexpr int KS = C::BK / 16, NR = C::TM + C::TN, NMF = C::TM * C::TN;
-    constexpr int VPER = (C::LPT + NMF - 1) / NMF, NV = (C::LPT + VPER - 1) / VPER;
-    static_assert(NR <= NMF && NV <= NMF, "schedule shape");
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int row = brow0 + j * 32;
+      fb[j] = *reinterpret_cast<const u32x4*>(bs + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
+    }
+  };
+  auto mfma_one = [&](int idx, const u32x4 (&fa)[C::TM], const u32x4 (&fb)[C::TN])
+      __attribute__((always_inline)) {
+    const int i = idx / C::TN, j = idx % C::TN;
+    acc[i][j] = TRANS ? mfma32x32x16<Tag>(fb[j], fa[i], acc[i][j])
+                      : mfma32x32x16<Tag>(fa[i], fb[j], acc[i][j]);
+  };
+
+  // Pipeline. Load group g carries K slice min(g, nk-1) into stage g % NS;
+  // groups 0..NS-1 go out first, then one more group per slice boundary. In
+  // the last k-step of slice kt, after a few MFMAs are queued, every wave
+  // waits for slice kt+1 (NS-2 younger groups may stay in flight) and meets
+  // at a barrier: slice kt+1 is then visible to all waves and the stage of
+  // slice kt is no longer read, so group kt+NS is issued into it and the
+  // first fragments of slice kt+1 are read under the remaining MFMAs of slice
+  // kt. Groups past the last slice re-read it into a stage nobody reads again
+  // (which keeps the group count, and so every vmcnt wait, uniform).
+#pragma unroll
+  for (int t = 0; t < C::NS; ++t) issue(min(t, nk - 1), t);
+  wait_vmcnt<(C::NS - 1) * C::LPT>();
+  __builtin_amdgcn_s_barrier();
+
+  constexpr int KS = C::BK / 16, NR = C::TM + C::TN, NMF = C::TM * C::TN;
+#ifndef MHA_GEMM_PRE
+#define MHA_GEMM_PRE 2
+#endif
+  // MFMAs of the last k-step queued before the barrier
+  constexpr int PRE = MHA_GEMM_PRE < NMF ? MHA_GEMM_PRE : NMF / 2;
+  static_assert(PRE >= 1 && PRE < NMF, "schedule shape");
+  constexpr int LB = (KS - 1) & 1;   // fragment buffer of the last k-step
+  u32x4 a[2][C::TM], b[2][C::TN];
+  // All k-steps of slice kt but the last, and the first PRE MFMAs of the last.
+  auto slice_head = [&](int kt) __attribute__((always_inline)) {
+    const uint8_t* as = smem + (kt % C::NS) * C::STAGE;
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
+      frags(as, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NMF - NR, 0);
+      for (int q = 0; q < NMF; ++q) mfma_one(q, a[ks & 1], b[ks & 1]);
     }
 #pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, VPER, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF - NV, 0);
+    for (int q = 0; q < PRE; ++q) mfma_one(q, a[LB], b[LB]);
+    // Issue order: the next k-step's reads go out one per MFMA over the first
+    // MFMAs, so the remaining ones cover their latency.
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) sched_run<NMF, NR, 0>();
+  };
+  frags(smem, 0, a[0], b[0]);
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    slice_head(kt);
+    // (sched_barrier: nothing may be moved across the wait and the barrier,
+    // MFMAs included, so exactly the MFMAs above are queued while waiting.)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(C::NS - 2) * C::LPT>();
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(min(kt + C::NS, nk - 1), kt % C::NS);
+    frags(smem + ((kt + 1) % C::NS) * C::STAGE, 0, a[0], b[0]);
+#pragma unroll
+    for (int q = PRE; q < NMF; ++q) mfma_one(q, a[LB], b[LB]);
+    // Reads of the next slice's first k-step first, then the new group's
+    // global->LDS loads, spread over the remaining MFMAs.
+    sched_run<NMF - PRE, NR, C::LPT>();
   }
+  slice_head(nk - 1);
+#pragma unroll
+  for (int q = PRE; q < NMF; ++q) mfma_one(q, a[LB], b[LB]);
   wait_vmcnt<0>();   // no global->LDS copy may outlive the workgroup
   // Every wave has finished reading the stages: each wave may now use its
   // share of the LDS to stage its output tile.
@@ -234,21 +274,11 @@ __device__ __forceinline__ int vt_pos(int t) {
 
 // Q and K columns (transposed tiles): a lane holds row m and channels
 // n..n+3. Q is scaled by q_scale; rows t < early_rows are also written in fp32.
+// Every tile goes through LDS: the wave's fp16 tile is staged row by row, then
+// written back 16 bytes per lane. Each 16-byte chunk is 8 channels of one
+// head at one position; runs of a head are contiguous in (B, h, T, d_k).
 struct QkEpi {
   QkvEpilogue e;
-
-  __device__ __forceinline__ void bias4(int ng, const f32x16_t& a, int r0, float (&v)[4]) const {
-    if (e.bias) {
-      const u32x2 bb = *reinterpret_cast<const u32x2*>(e.bias + ng);
-      v[0] = a[r0 + 0] + __uint_as_float(bb.x << 16);
-      v[1] = a[r0 + 1] + __uint_as_float(bb.x & 0xffff0000u);
-      v[2] = a[r0 + 2] + __uint_as_float(bb.y << 16);
-      v[3] = a[r0 + 3] + __uint_as_float(bb.y & 0xffff0000u);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = a[r0 + r];
-    }
-  }
 
   template <int TM, int TN>
   __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
@@ -256,72 +286,96 @@ struct QkEpi {
     constexpr int WM = TM * 32, WN = TN * 32, RB = WN * 2, CPR = WN / 8;
     const int D = e.D, d_k = e.d_k, T = e.T, lq = lane & 31, lh = lane >> 5;
     const int bw = mbase / T, tw = mbase - bw * T;
-    const bool staged = tw + WM <= T && mbase + WM <= M && nbase + WN <= N;
-    const bool early = e.early && tw < e.early_rows;
-    if (staged) {
-      // The wave's WN columns lie in one of Q or K (WN divides D).
-      const int ng0 = e.n_base + nbase, which = ng0 / D, hc0 = ng0 - which * D;
-      const float sc = which == 0 ? e.q_scale : 1.0f;
+    // The wave's WN columns lie in one of Q or K (WN divides D).
+    const int ng0 = e.n_base + nbase, which = ng0 / D, hc0 = ng0 - which * D;
+    const float sc = which == 0 ? e.q_scale : 1.0f;
+    // The wave's bias values, fetched together (one latency, not one per
+    // fragment): lane columns ng0 + 32 j + 8 rg + 4 lh + 0..3 (clamped to the
+    // last column; values past N are never stored).
+    u32x2 bb[TN][4];
+    if (e.bias) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          bb[j][rg] = *reinterpret_cast<const u32x2*>(
+              e.bias + e.n_base + min(nbase + j * 32 + 8 * rg + 4 * lh, N - 4));
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) bb[j][rg] = u32x2{0u, 0u};
+    }
+    auto biased = [&](int i, int j, int rg, float (&v)[4]) __attribute__((always_inline)) {
+      const f32x16_t& a = acc[i][j];
+      const u32x2 b2 = bb[j][rg];
+      v[0] = a[rg * 4 + 0] + __uint_as_float(b2.x << 16);
+      v[1] = a[rg * 4 + 1] + __uint_as_float(b2.x & 0xffff0000u);
+      v[2] = a[rg * 4 + 2] + __uint_as_float(b2.y << 16);
+      v[3] = a[rg * 4 + 3] + __uint_as_float(b2.y & 0xffff0000u);
+    };
+    // Rows t < early_rows also go out in fp32 (tiles holding such rows only).
+    if (e.early && (tw < e.early_rows || tw + WM > T)) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int r = i * 32 + lq;
+        const int m = mbase + i * 32 + lq;
+        const int b = m / T, t = m - b * T;
+        if (m < M && t < e.early_rows) {
+          float* er = e.early + ((size_t)b * e.early_rows + t) * (3 * D) + ng0;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const int c = j * 32 + 8 * rg + 4 * lh;
-            float v[4];
-            bias4(ng0 + c, acc[i][j], rg * 4, v);
-            if (early && tw + r < e.early_rows)
-              *reinterpret_cast<f32x4_t*>(e.early + ((size_t)bw * e.early_rows + tw + r) * (3 * D) +
-                                          ng0 + c) = f32x4_t{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<u32x2*>(lds + r * RB + stage_chunk<RB>(r, c >> 3) * 16 + lh * 8) =
-                u32x2{pack_f16x2(v[0] * sc, v[1] * sc), pack_f16x2(v[2] * sc, v[3] * sc)};
-          }
-      }
-      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
-      // Write-back: chunk runs of one head are contiguous in (B, h, T, d_k).
-      const int hseg = min(WN, d_k), lg_cph = hseg == 128 ? 4 : 3;   // chunks per head segment
-      const int tpad = which == 0 ? e.Tpad_q : e.Tpad_kv;
-      uint16_t* base = (which == 0 ? e.q : e.k) + (size_t)bw * e.h * tpad * d_k;
-#pragma unroll 4
-      for (int k = 0; k < WM * CPR / 64; ++k) {
-        const int idx = k * 64 + lane;
-        const int cb = idx >> (lg_cph + __builtin_ctz(WM)), rem = idx & ((WM << lg_cph) - 1);
-        const int r = rem >> lg_cph, c8 = (cb << lg_cph) + (rem & ((1 << lg_cph) - 1));
-        const u32x4 val = *reinterpret_cast<const u32x4*>(lds + r * RB + stage_chunk<RB>(r, c8) * 16);
-        const int col = hc0 + c8 * 8, head = col / d_k, ch = col - head * d_k;
-        *reinterpret_cast<u32x4*>(base + ((size_t)head * tpad + tw + r) * d_k + ch) = val;
-      }
-      return;
-    }
-    // Direct path: 8-byte stores of four channels.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = mbase + i * 32 + lq;
-      if (m >= M) continue;
-      const int b = m / T, t = m - b * T;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int n = nbase + j * 32 + 8 * rg + 4 * lh;   // four columns n..n+3
-          if (n >= N) continue;
-          const int ng = e.n_base + n;
-          const int which = ng / D, hc = ng - which * D, head = hc / d_k, c = hc - head * d_k;
-          float v[4];
-          bias4(ng, acc[i][j], rg * 4, v);
-          if (e.early && t < e.early_rows)
-            *reinterpret_cast<f32x4_t*>(e.early + ((size_t)b * e.early_rows + t) * (3 * D) + ng) =
-                f32x4_t{v[0], v[1], v[2], v[3]};
-          const float sc = which == 0 ? e.q_scale : 1.0f;
-          const int tpad = which == 0 ? e.Tpad_q : e.Tpad_kv;
-          uint16_t* dst = (which == 0 ? e.q : e.k) +
-                          (((size_t)b * e.h + head) * tpad + t) * d_k + c;
-          *reinterpret_cast<u32x2*>(dst) =
-              u32x2{pack_f16x2(v[0] * sc, v[1] * sc), pack_f16x2(v[2] * sc, v[3] * sc)};
+            for (int rg = 0; rg < 4; ++rg) {
+              const int c = j * 32 + 8 * rg + 4 * lh;
+              if (nbase + c < N) {
+                float v[4];
+                biased(i, j, rg, v);
+                *reinterpret_cast<f32x4_t*>(er + c) = f32x4_t{v[0], v[1], v[2], v[3]};
+              }
+            }
         }
       }
+    }
+    // fp16 tile into LDS, one 32-row block at a time (the scheduling fence
+    // keeps the compiler from hoisting every block's accumulator reads).
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = i * 32 + lq;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int c = j * 32 + 8 * rg + 4 * lh;
+          float v[4];
+          biased(i, j, rg, v);
+          *reinterpret_cast<u32x2*>(lds + r * RB + stage_chunk<RB>(r, c >> 3) * 16 + lh * 8) =
+              u32x2{pack_f16x2(v[0] * sc, v[1] * sc), pack_f16x2(v[2] * sc, v[3] * sc)};
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+    // Write-back. Chunk order: head segment, row, chunk within the segment,
+    // so consecutive lanes cover contiguous memory.
+    const int hseg = min(WN, d_k), lg_cph = hseg == 128 ? 4 : 3;   // chunks per head segment
+    const int tpad = which == 0 ? e.Tpad_q : e.Tpad_kv;
+    uint16_t* const dst = which == 0 ? e.q : e.k;
+    const bool simple = tw + WM <= T && mbase + WM <= M && nbase + WN <= N;
+#pragma unroll 4
+    for (int k = 0; k < WM * CPR / 64; ++k) {
+      const int idx = k * 64 + lane;
+      const int cb = idx >> (lg_cph + __builtin_ctz(WM)), rem = idx & ((WM << lg_cph) - 1);
+      const int r = rem >> lg_cph, c8 = (cb << lg_cph) + (rem & ((1 << lg_cph) - 1));
+      const u32x4 val = *reinterpret_cast<const u32x4*>(lds + r * RB + stage_chunk<RB>(r, c8) * 16);
+      const int col = hc0 + c8 * 8, head = col / d_k, ch = col - head * d_k;
+      int b = bw, t = tw + r;
+      if (!simple) {   // tile crosses a sequence end or the matrix edge
+        const int m = mbase + r;
+        if (m >= M || nbase + c8 * 8 >= N) continue;
+        b = m / T;
+        t = m - b * T;
+      }
+      __builtin_nontemporal_store(
+          val, reinterpret_cast<u32x4*>(dst + (((size_t)b * e.h + head) * tpad + t) * d_k + ch));
     }
   }
 };
@@ -341,11 +395,19 @@ struct VEpi {
     const bool staged = (tw & 15) == 0 && tw + WM <= T && mbase + WM <= M && nbase + WN <= N;
     if (staged) {
       const int hc0 = e.n_base + nbase - 2 * D;
+      float bj[TN];   // the wave's bias values, fetched together
+      if (e.bias) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bj[j] = bf16_bits_to_float(e.bias[e.n_base + nbase + j * 32 + lq]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bj[j] = 0.0f;
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int c = j * 32 + lq;
         const int ng = e.n_base + nbase + c;
-        const float bias = load_bias_bf16(e.bias, ng);
+        const float bias = bj[j];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -374,8 +436,9 @@ struct VEpi {
         const int c = idx / CPR, p8 = idx - c * CPR;
         const u32x4 val = *reinterpret_cast<const u32x4*>(lds + c * RB + stage_chunk<RB>(c, p8) * 16);
         const int col = hc0 + c, head = col / d_k, ch = col - head * d_k;
-        *reinterpret_cast<u32x4*>(e.vt + (((size_t)bw * e.h + head) * d_k + ch) * e.Tpad_kv + tw +
-                                  p8 * 8) = val;
+        __builtin_nontemporal_store(
+            val, reinterpret_cast<u32x4*>(e.vt + (((size_t)bw * e.h + head) * d_k + ch) * e.Tpad_kv +
+                                          tw + p8 * 8));
       }
       return;
     }
@@ -411,25 +474,50 @@ struct VEpi {
   }
 };
 
-// fp32 result epilogue of the output projection.
+// fp32 result epilogue of the output projection, on transposed tiles: a lane
+// holds row m and four consecutive columns n..n+3 per fragment group, which
+// go out as one 16-byte store (four stores cover a 128-byte line of a row).
 struct OutEpi {
   const uint16_t* bias;
   float* Y;
   template <int TM, int TN>
   __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
                                         int M, int N, uint8_t* /*lds*/) const {
+    const int lq = lane & 31, lh = lane >> 5;
+    // The wave's bias values, fetched together (clamped to the last columns;
+    // values past N are never stored).
+    u32x2 bb[TN][4];
+    if (bias) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = nbase + j * 32 + (lane & 31);
-      if (n >= N) continue;
-      const float b = load_bias_bf16(bias, n);
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int rg = 0; rg < 4; ++rg)
+          bb[j][rg] = *reinterpret_cast<const u32x2*>(bias + min(nbase + j * 32 + 8 * rg + 4 * lh, N - 4));
+    } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mbase + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (m < M) Y[(size_t)m * N + n] = acc[i][j][r] + b;
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) bb[j][rg] = u32x2{0u, 0u};
+    }
+    const bool full = mbase + TM * 32 <= M && nbase + TN * 32 <= N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mbase + i * 32 + lq;
+      float* yr = Y + (size_t)m * N + nbase;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int c = j * 32 + 8 * rg + 4 * lh;
+          const f32x16_t& a = acc[i][j];
+          const u32x2 b2 = bb[j][rg];
+          const f32x4_t v = {a[rg * 4 + 0] + __uint_as_float(b2.x << 16),
+                             a[rg * 4 + 1] + __uint_as_float(b2.x & 0xffff0000u),
+                             a[rg * 4 + 2] + __uint_as_float(b2.y << 16),
+                             a[rg * 4 + 3] + __uint_as_float(b2.y & 0xffff0000u)};
+          if (full || (m < M && nbase + c < N)) *reinterpret_cast<f32x4_t*>(yr + c) = v;
         }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
@@ -566,10 +654,10 @@ hipError_t launch_gemm_out(const uint16_t* A, int M, int K, const uint16_t* Bt, 
                            const uint16_t* bias, float* Y, hipStream_t s) {
   OutEpi epi{bias, Y};
   if (use_big(M, N))
-    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, false, OutEpi>), dim3(tiles_of(M, N, 256, 256)),
+    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi>), dim3(tiles_of(M, N, 256, 256)),
                        dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
   else
-    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, false, OutEpi>), dim3(tiles_of(M, N, 128, 128)),
+    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, true, OutEpi>), dim3(tiles_of(M, N, 128, 128)),
                        dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K, epi);
   return hipGetLastError();
 }
