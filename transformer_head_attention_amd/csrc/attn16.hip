@@ -219,7 +219,20 @@ attn_f16_kernel(AttnF16Args a) {
       bits = (((uint64_t)mask_s[stage][1] << 32) | mask_s[stage][0]) >> (4 * lh);
     const bool masked_tile = HAS_MASK || tail;
 
-    // Phase 1: S'^T = K . Q^T - base for every live query tile.
+    // Phase 1: S'^T = K . Q^T - base for every live query tile. All K
+    // fragments of the tile are read before the first MFMA (one LDS latency
+    // per tile instead of one per MFMA), and all V^T fragments right after
+    // the MFMAs, so they arrive while the softmax runs.
+    u32x4 kf[2][KSTEPS];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int row = kh * 32 + lq;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        kf[kh][ks] = *reinterpret_cast<const u32x4*>(
+            Ks + (row * KCH + swz<KCH>(row, 2 * ks + lh)) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x16_t s[NQ][2];
     bool live[NQ];
 #pragma unroll
@@ -232,15 +245,21 @@ attn_f16_kernel(AttnF16Args a) {
       for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[qi][kh][r] = init;
-        const int row = kh * 32 + lq;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(
-              Ks + (row * KCH + swz<KCH>(row, 2 * ks + lh)) * 16);
-          s[qi][kh] = mfma32x32x16<F16>(kf, qreg[qi][ks], s[qi][kh]);
-        }
+        for (int ks = 0; ks < KSTEPS; ++ks)
+          s[qi][kh] = mfma32x32x16<F16>(kf[kh][ks], qreg[qi][ks], s[qi][kh]);
       }
     }
+    u32x4 vf[DT][4];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int row = dt * 32 + lq;
+      const uint8_t* vrow = Vs + row * 128;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        vf[dt][c] = *reinterpret_cast<const u32x4*>(vrow + swz<8>(row, 2 * c + lh) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // Phase 2 (per query tile): mask, lazy reference update, P = exp2(S'),
     // then O^T += V^T . P^T.
@@ -305,15 +324,9 @@ attn_f16_kernel(AttnF16Args a) {
       // P^T fragment c covers keys c*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}; V^T
       // row d supplies the same keys as its chunk 2c + lh.
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int row = dt * 32 + lq;
-        const uint8_t* vrow = Vs + row * 128;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + swz<8>(row, 2 * c + lh) * 16);
-          o[qi][dt] = mfma32x32x16<F16>(vf, pf[c], o[qi][dt]);
-        }
-      }
+        for (int c = 0; c < 4; ++c) o[qi][dt] = mfma32x32x16<F16>(vf[dt][c], pf[c], o[qi][dt]);
     }
   }
 

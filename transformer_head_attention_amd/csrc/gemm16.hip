@@ -526,22 +526,25 @@ struct OutEpi {
 // fp32 attention output: Y[b*T_q + t] = O32[b*R + t] . W_O + b_O for t < R.
 // Each fp32 value x is split into fp16 hi = fp16(x) and lo = fp16(x - hi), and
 // hi . W + lo . W is accumulated in fp32 on the fp16 MFMA, which keeps about
-// 22 significant bits of x. A workgroup owns a 32 x 32 tile of Y; its four
-// waves take a quarter of K each and are summed through LDS in a fixed order.
-__global__ void __launch_bounds__(256)
+// 22 significant bits of x. A workgroup owns a 32 x 32 tile of Y; its eight
+// waves take an eighth of K each (all of a wave's loads are in flight at
+// once) and are summed through LDS in a fixed order.
+constexpr int EO_WAVES = 8;
+
+__global__ void __launch_bounds__(EO_WAVES * 64)
 early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __restrict__ WoT,
                  int N, const uint16_t* __restrict__ bias, float* __restrict__ Y, int R, int T_q) {
-  __shared__ f32x16_t red[3][64];
+  __shared__ f32x16_t red[EO_WAVES - 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
-  const int kw = K / 4, kbeg = wave * kw;
+  const int kw = K / EO_WAVES, kbeg = wave * kw;
   const int row = min(m0 + (lane & 31), M - 1);
   const float* ap = O32 + (size_t)row * K + (lane >> 5) * 8;
   const uint16_t* bp = WoT + (size_t)(n0 + (lane & 31)) * K + (lane >> 5) * 8;
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll 4
+#pragma unroll 8
   for (int k = kbeg; k < kbeg + kw; k += 16) {
     const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(ap + k);
     const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(ap + k + 4);
@@ -562,7 +565,7 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 0; w < 3; ++w) acc += red[w][lane];
+  for (int w = 0; w < EO_WAVES - 1; ++w) acc += red[w][lane];
   const int n = n0 + (lane & 31);
   const float bv = load_bias_bf16(bias, n);
 #pragma unroll
@@ -646,7 +649,8 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
 hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
                             const uint16_t* bias, float* Y, int R, int T_q, hipStream_t s) {
   dim3 grid(N / 32, (M + 31) / 32);
-  hipLaunchKernelGGL(early_out_kernel, grid, dim3(256), 0, s, O32, M, K, WoT, N, bias, Y, R, T_q);
+  hipLaunchKernelGGL(early_out_kernel, grid, dim3(EO_WAVES * 64), 0, s, O32, M, K, WoT, N, bias, Y, R,
+                     T_q);
   return hipGetLastError();
 }
 

@@ -81,5 +81,7 @@ struct AttnF32Args {
   int B, h, rows, T_k, causal;                 // rows = query rows evaluated (t = 0..rows-1)
 };
 hipError_t launch_attn_f32(const AttnF32Args& a, int d_k, hipStream_t s);
+// rows <= T_k <= 64 (the first rows of causal sequences).
+hipError_t launch_attn_early(const AttnF32Args& a, int d_k, hipStream_t s);
 
 }  // namespace mha

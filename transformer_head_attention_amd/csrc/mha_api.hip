@@ -341,7 +341,7 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
       f.rows = L.R;
       f.T_k = L.R;
       f.causal = 1;
-      MHA_HIP(mha::launch_attn_f32(f, d_k, s));
+      MHA_HIP(mha::launch_attn_early(f, d_k, s));
       MHA_HIP(mha::launch_early_out(eo, B * L.R, D, woT, D, static_cast<const uint16_t*>(b_o), y,
                                     L.R, T_q, s));
     }

@@ -10,28 +10,39 @@ namespace {
 
 constexpr int TT = 64;   // transpose tile edge
 
-// WT[n][k] = W[k][n]; one 64 x 64 tile per workgroup, 256 threads.
+// WT[n][k] = W[k][n]; one 64 x 64 tile per workgroup, 256 threads. Global
+// traffic moves 16 bytes per lane both ways: rows of W are read as 8-element
+// chunks, and each output chunk gathers 8 consecutive k of one column from
+// LDS (rows padded by 16 bytes, so the 8 lanes gathering one column chunk
+// hit different banks). Requires K and N to be multiples of 8.
 template <bool TO_F16>
 __global__ void __launch_bounds__(256)
 transpose_bf16_kernel(const uint16_t* __restrict__ W, int K, int N, uint16_t* __restrict__ WT) {
-  __shared__ uint16_t tile[TT][TT + 2];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TT][TT + 8];
   const int n0 = blockIdx.x * TT, k0 = blockIdx.y * TT;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int t = threadIdx.x, r = t >> 3, c = t & 7;
 #pragma unroll
-  for (int i = 0; i < TT / 4; ++i) {
-    const int kr = ty + 4 * i;
-    const int k = k0 + kr, n = n0 + tx;
-    tile[kr][tx] = (k < K && n < N) ? W[(size_t)k * N + n] : (uint16_t)0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int kr = r + 32 * pass, k = k0 + kr, n = n0 + 8 * c;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k < K && n < N) v = *reinterpret_cast<const u32x4*>(W + (size_t)k * N + n);
+    *reinterpret_cast<u32x4*>(&tile[kr][8 * c]) = v;
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < TT / 4; ++i) {
-    const int nr = ty + 4 * i;
-    const int n = n0 + nr, k = k0 + tx;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nr = r + 32 * pass, n = n0 + nr, k = k0 + 8 * c;
     if (n < N && k < K) {
-      uint16_t v = tile[tx][nr];
-      if (TO_F16) v = float_to_f16_bits(bf16_bits_to_float(v));
-      WT[(size_t)n * K + k] = v;
+      uint16_t e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint16_t v = tile[8 * c + j][nr];
+        if (TO_F16) v = float_to_f16_bits(bf16_bits_to_float(v));
+        e[j] = v;
+      }
+      *reinterpret_cast<u32x4*>(WT + (size_t)n * K + k) =
+          u32x4{e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16};
     }
   }
 }
