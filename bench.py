@@ -9,8 +9,9 @@ the fp32 early-row pass), inputs resident in HBM. Prints one JSON line.
 
 Beside the headline rate the line carries:
   roofline      the dominant kernel's algorithmic FLOPs per launch divided by
-                its average launch time (HIP events on the launch stream,
-                around each of the timed calls), against the MI355X dense
+                its average launch time (HIP events on the launch stream
+                around that stage, over a second pass of K steps, so the
+                event records do not perturb the timed steps), against the MI355X dense
                 fp16/bf16 MFMA peak; `traffic` is the HBM bytes per launch from
                 the committed rocprofv3 counter summary, or null when that
                 summary was taken on a different kernel source.
@@ -127,8 +128,8 @@ def copy_calibration(torch, steps: int) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -160,11 +161,14 @@ def main() -> int:
                   causal=w.causal, key_padding_mask=t["key_padding_mask"], out=y, workspace=ws,
                   stream=stream.cuda_stream)
 
+    # Untimed warmup: the first few hundred microseconds of sustained work
+    # run at a different clock than the steady state that follows.
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    mha._check(mha.mha_profile_begin(m.handle, args.steps), "mha_profile_begin")
+    # Timed region: K steps bracketed by events on the launch stream, with no
+    # other events inside (an event record between kernels costs ~5 us).
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -174,6 +178,13 @@ def main() -> int:
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+
+    # Per-stage times: K more steps with the library's stage events (HIP
+    # events on the same stream around each stage's kernels).
+    mha._check(mha.mha_profile_begin(m.handle, args.steps), "mha_profile_begin")
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     st, stages, ncalls = mha.mha_profile_end(m.handle)
     mha._check(st, "mha_profile_end")
 

@@ -283,11 +283,16 @@ attn_f16_kernel(AttnF16Args a) {
           }
       }
 
-      float mx = s[qi][0][0];
+      // Row maximum as four independent chains (short dependency depth).
+      float m4[4];
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qi][kh][r]);
+      for (int g = 0; g < 4; ++g) {
+        const f32x16_t& sv = s[qi][g >> 1];
+        const int r0 = (g & 1) * 8;
+        m4[g] = fmaxf(fmaxf(fmaxf(sv[r0], sv[r0 + 1]), fmaxf(sv[r0 + 2], sv[r0 + 3])),
+                      fmaxf(fmaxf(sv[r0 + 4], sv[r0 + 5]), fmaxf(sv[r0 + 6], sv[r0 + 7])));
+      }
+      float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
       mx = pair32_max(mx);
       const bool first = !seen[qi] && mx != -INFINITY;
       const float shift = first ? mx : (mx > 8.0f ? mx : 0.0f);
@@ -306,20 +311,19 @@ attn_f16_kernel(AttnF16Args a) {
       }
       seen[qi] = seen[qi] || first;
 
-      float rs = 0.0f;
+      // Row sum as a tree per fragment group (short dependency depth).
+      float rs4[4];
       u32x4 pf[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(s[qi][c >> 1][(c & 1) * 8 + e]);
-          rs += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[qi][c >> 1][(c & 1) * 8 + e]);
+        rs4[c] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pf[c] = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]),
                       pack_f16x2(p[4], p[5]), pack_f16x2(p[6], p[7])};
       }
-      l_run[qi] += rs;
+      l_run[qi] += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
 
       // P^T fragment c covers keys c*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}; V^T
       // row d supplies the same keys as its chunk 2c + lh.

@@ -172,7 +172,9 @@ mha_status_t mha_profile_begin(mha_handle_t hd, int max_calls) {
   if (!hd || max_calls < 1) return MHA_ERR_INVALID_ARG;
   for (hipEvent_t e : hd->prof_ev) (void)hipEventDestroy(e);
   hd->prof_ev.assign((size_t)max_calls * (MHA_NUM_STAGES + 1), nullptr);
-  for (auto& e : hd->prof_ev) MHA_HIP(hipEventCreate(&e));
+  // Timing-only events: no system-scope fence (no cache write-back and
+  // invalidation at every stage boundary, which would perturb what is timed).
+  for (auto& e : hd->prof_ev) MHA_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   hd->prof_max = max_calls;
   hd->prof_calls = 0;
   return MHA_OK;
