@@ -582,16 +582,16 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
 // AGPRs, one wave per SIMD). Problems with too few such tiles to fill the
 // 256 CUs use 128 x 128 tiles, four waves of 64 x 64.
 #ifndef MHA_BIG_BK
-#define MHA_BIG_BK 32
+#define MHA_BIG_BK 64
 #endif
 #ifndef MHA_BIG_NS
-#define MHA_BIG_NS 4
+#define MHA_BIG_NS 2
 #endif
 #ifndef MHA_SMALL_BK
-#define MHA_SMALL_BK 32
+#define MHA_SMALL_BK 64
 #endif
 #ifndef MHA_SMALL_NS
-#define MHA_SMALL_NS 4
+#define MHA_SMALL_NS 2
 #endif
 using BigCfg = Cfg<256, 256, 128, 128, MHA_BIG_BK, MHA_BIG_NS>;
 using SmallCfg = Cfg<128, 128, 64, 64, MHA_SMALL_BK, MHA_SMALL_NS>;
