@@ -113,7 +113,7 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   // groups of GM row bands so that the concurrently resident workgroups of
   // an XCD share A rows and B columns in its L2.
 #ifndef MHA_GEMM_GM
-#define MHA_GEMM_GM 4
+#define MHA_GEMM_GM 8
 #endif
   constexpr int GM = MHA_GEMM_GM;
   const int ntn = (N + C::BN - 1) / C::BN, ntm = (M + C::BM - 1) / C::BM;
