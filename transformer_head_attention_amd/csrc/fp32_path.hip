@@ -216,18 +216,26 @@ attn_early_kernel(AttnF32Args a) {
   const bool valid = t < a.rows;
   const int kend = a.causal ? min(a.T_k, blockIdx.x * ER + ER) : a.T_k;   // <= 64 (host-checked)
 
+  // Keys [0, kend) of this head; rows past kend are zero so that the key
+  // loops below can run over all 64 rows without branches (their weights
+  // are exactly 0 and 0 * 0 stays 0).
   const float* kb = a.k + (size_t)b * a.kv_bstride + head * DK;
   const float* vb = a.v + (size_t)b * a.kv_bstride + head * DK;
-  for (int idx = tid; idx < kend * (DK / 4); idx += 256) {
+  for (int idx = tid; idx < 64 * (DK / 4); idx += 256) {
     const int key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
-    *reinterpret_cast<f32x4_t*>(&Ks[key][c4]) =
-        *reinterpret_cast<const f32x4_t*>(kb + (size_t)key * a.kv_ld + c4);
-    *reinterpret_cast<f32x4_t*>(&Vs[key][c4]) =
-        *reinterpret_cast<const f32x4_t*>(vb + (size_t)key * a.kv_ld + c4);
+    f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
+    if (key < kend) {
+      kv = *reinterpret_cast<const f32x4_t*>(kb + (size_t)key * a.kv_ld + c4);
+      vv = *reinterpret_cast<const f32x4_t*>(vb + (size_t)key * a.kv_ld + c4);
+    }
+    *reinterpret_cast<f32x4_t*>(&Ks[key][c4]) = kv;
+    *reinterpret_cast<f32x4_t*>(&Vs[key][c4]) = vv;
   }
   if (tid < 64) Ms[tid] = (a.mask && tid < kend) ? a.mask[(size_t)b * a.mask_ld + tid] : 0;
 
-  const float scale = 1.0f / sqrtf((float)DK);
+  // Scores in log2 units: q is pre-multiplied by log2(e) / sqrt(d_k), so the
+  // softmax is exp2(s - max) (the same weights as exp(qk/sqrt(d_k) - max)).
+  const float scale = 1.4426950408889634f / sqrtf((float)DK);
   float q[CPL];
   const float* qp = a.q + (size_t)b * a.q_bstride + (size_t)(valid ? t : 0) * a.q_ld + head * DK +
                     p * CPL;
@@ -238,21 +246,22 @@ attn_early_kernel(AttnF32Args a) {
     for (int e = 0; e < 4; ++e) q[c + e] = v[e] * scale;
   }
   __syncthreads();
+  // Ignored keys of this row as a bitmask: past the extent, in the future
+  // (causal) or flagged in the padding mask.
+  const uint64_t padm = __ballot(Ms[lane] != 0);
+  const int seen_keys = a.causal ? min(kend, t + 1) : kend;
+  const uint64_t live = (seen_keys >= 64 ? ~0ull : ((1ull << max(seen_keys, 0)) - 1)) & ~padm;
 
   float sc[64];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 64; ++j) {
-    sc[j] = -INFINITY;
-    if (j < kend) {
-      float part = 0.0f;
+    float part = 0.0f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) part = __builtin_fmaf(q[c], Ks[j][p * CPL + c], part);
-      part = row16_sum(part);
-      const bool ign = (a.causal && j > t) || Ms[j] != 0;
-      sc[j] = ign ? -INFINITY : part;
-      mx = fmaxf(mx, sc[j]);
-    }
+    for (int c = 0; c < CPL; ++c) part = __builtin_fmaf(q[c], Ks[j][p * CPL + c], part);
+    part = row16_sum(part);
+    sc[j] = ((live >> j) & 1ull) ? part : -INFINITY;
+    mx = fmaxf(mx, sc[j]);
   }
   const float base = mx == -INFINITY ? 0.0f : mx;
   float l = 0.0f, o[CPL];
@@ -260,12 +269,10 @@ attn_early_kernel(AttnF32Args a) {
   for (int c = 0; c < CPL; ++c) o[c] = 0.0f;
 #pragma unroll
   for (int j = 0; j < 64; ++j) {
-    if (j < kend) {
-      const float pj = expf(sc[j] - base);
-      l += pj;
+    const float pj = __builtin_amdgcn_exp2f(sc[j] - base);
+    l += pj;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) o[c] = __builtin_fmaf(pj, Vs[j][p * CPL + c], o[c]);
-    }
+    for (int c = 0; c < CPL; ++c) o[c] = __builtin_fmaf(pj, Vs[j][p * CPL + c], o[c]);
   }
   if (valid) {
     float* op = a.o + (size_t)b * a.o_bstride + (size_t)t * a.o_ld + head * DK + p * CPL;

@@ -15,6 +15,8 @@
 // with v_mfma_f32_32x32x16.
 #include <utility>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -526,10 +528,10 @@ struct OutEpi {
 // fp32 attention output: Y[b*T_q + t] = O32[b*R + t] . W_O + b_O for t < R.
 // Each fp32 value x is split into fp16 hi = fp16(x) and lo = fp16(x - hi), and
 // hi . W + lo . W is accumulated in fp32 on the fp16 MFMA, which keeps about
-// 22 significant bits of x. A workgroup owns a 32 x 32 tile of Y; its eight
-// waves take an eighth of K each (all of a wave's loads are in flight at
-// once) and are summed through LDS in a fixed order.
-constexpr int EO_WAVES = 8;
+// 22 significant bits of x. A workgroup owns a 32 x 32 tile of Y; its four
+// waves take a quarter of K each (loads issued in batches of k-steps, each
+// batch before its MFMAs) and are summed through LDS in a fixed order.
+constexpr int EO_WAVES = 4;
 
 __global__ void __launch_bounds__(EO_WAVES * 64)
 early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __restrict__ WoT,
@@ -544,23 +546,41 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll 8
-  for (int k = kbeg; k < kbeg + kw; k += 16) {
-    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(ap + k);
-    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(ap + k + 4);
-    const u32x4 bf = *reinterpret_cast<const u32x4*>(bp + k);
-    const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    uint32_t hi[4], lo[4];
+  // NB k-steps at a time: all of their loads go out before the first MFMA,
+  // so a batch costs one memory latency.
+  auto batch = [&](auto nb_tag, int k) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb_tag)::value;
+    f32x4_t a0[NB], a1[NB];
+    u32x4 bf[NB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const _Float16 h0 = static_cast<_Float16>(av[2 * e]);
-      const _Float16 h1 = static_cast<_Float16>(av[2 * e + 1]);
-      hi[e] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
-      lo[e] = pack_f16x2(av[2 * e] - static_cast<float>(h0), av[2 * e + 1] - static_cast<float>(h1));
+    for (int s = 0; s < NB; ++s) {
+      a0[s] = *reinterpret_cast<const f32x4_t*>(ap + k + 16 * s);
+      a1[s] = *reinterpret_cast<const f32x4_t*>(ap + k + 16 * s + 4);
+      bf[s] = *reinterpret_cast<const u32x4*>(bp + k + 16 * s);
     }
-    acc = mfma32x32x16<F16>(u32x4{hi[0], hi[1], hi[2], hi[3]}, bf, acc);
-    acc = mfma32x32x16<F16>(u32x4{lo[0], lo[1], lo[2], lo[3]}, bf, acc);
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const float av[8] = {a0[s][0], a0[s][1], a0[s][2], a0[s][3],
+                           a1[s][0], a1[s][1], a1[s][2], a1[s][3]};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const _Float16 h0 = static_cast<_Float16>(av[2 * e]);
+        const _Float16 h1 = static_cast<_Float16>(av[2 * e + 1]);
+        hi[e] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
+        lo[e] = pack_f16x2(av[2 * e] - static_cast<float>(h0), av[2 * e + 1] - static_cast<float>(h1));
+      }
+      acc = mfma32x32x16<F16>(u32x4{hi[0], hi[1], hi[2], hi[3]}, bf[s], acc);
+      acc = mfma32x32x16<F16>(u32x4{lo[0], lo[1], lo[2], lo[3]}, bf[s], acc);
+    }
+  };
+  int k = kbeg;
+  for (; k + 16 * 8 <= kbeg + kw; k += 16 * 8) batch(std::integral_constant<int, 8>{}, k);
+  if (k + 16 * 4 <= kbeg + kw) {
+    batch(std::integral_constant<int, 4>{}, k);
+    k += 16 * 4;
   }
+  for (; k < kbeg + kw; k += 16) batch(std::integral_constant<int, 1>{}, k);
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
