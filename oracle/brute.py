@@ -11,6 +11,9 @@ library and no max-shift, so it shares no arithmetic shape with
 * A_ij = exp(s_ij) / sum_m exp(s_im) (same page, §10); all keys masked gives
   0/0, returned as NaN (molayo1419.me "MHA란 무엇인가?", trap 3).
 * o_i = sum_j A_ij v_j (§13); concat over heads and y = o W_O + b_O (§18).
+* With n_g key/value sets (itwiki, 추론 비용과 변형, variants table), query
+  head i takes its keys and values from set i // (h / n_g): columns
+  D + g*d_k ... of the K block and D + n_g*d_k + g*d_k ... of the V block.
 """
 
 from __future__ import annotations
@@ -32,10 +35,12 @@ def _matvec(x, w, col0, ncol, b):
 
 
 def brute_force_mha(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
-                    key_padding_mask=None):
+                    key_padding_mask=None, n_kv_heads=None):
     """Nested lists in, nested list Y[b][t][c] out. Inputs are plain floats."""
     D = len(w_qkv)
     d = D // h
+    n_g = h if n_kv_heads is None else n_kv_heads
+    per_group = h // n_g
     B = len(x_q)
     src = x_q if x_kv is None else x_kv
     y_all = []
@@ -45,6 +50,7 @@ def brute_force_mha(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
         for i in range(Tq):
             o_cat = []
             for head in range(h):
+                g = head // per_group
                 q = _matvec(x_q[b][i], w_qkv, head * d, d, b_qkv)
                 weights = []
                 for j in range(Tk):
@@ -53,7 +59,7 @@ def brute_force_mha(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
                     if masked:
                         weights.append(0.0)          # exp(-inf)
                         continue
-                    k = _matvec(src[b][j], w_qkv, D + head * d, d, b_qkv)
+                    k = _matvec(src[b][j], w_qkv, D + g * d, d, b_qkv)
                     s = sum(q[c] * k[c] for c in range(d)) / math.sqrt(d)
                     weights.append(math.exp(s))
                 total = sum(weights)
@@ -61,7 +67,7 @@ def brute_force_mha(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
                 for j in range(Tk):
                     if weights[j] == 0.0:
                         continue
-                    v = _matvec(src[b][j], w_qkv, 2 * D + head * d, d, b_qkv)
+                    v = _matvec(src[b][j], w_qkv, D + n_g * d + g * d, d, b_qkv)
                     for c in range(d):
                         o[c] += weights[j] * v[c]
                 if total == 0.0:

@@ -21,6 +21,11 @@ Sources (pages as titled; sections / equations named, no line numbers):
   sequence and K, V from the source sequence.
 * molayo1419.me "MHA란 무엇인가?", trap 2: key_padding_mask True = ignore
   this key; trap 3: a row whose keys are all ignored becomes 0/0 = NaN.
+* itwiki "멀티 헤드 어텐션", 추론 비용과 변형 (variants table): MQA keeps n_h
+  query heads and one key/value set shared by every head; GQA keeps n_g
+  key/value sets, each shared by a group of query heads; the key/value
+  elements per token and layer are 2 n_h d_h (MHA), 2 d_h (MQA), 2 n_g d_h
+  (GQA).
 
 Conventions (readings where the pages leave a step open):
 
@@ -28,6 +33,11 @@ Conventions (readings where the pages leave a step open):
   [Q | K | V]; inside each block head i owns columns [i*d_k, (i+1)*d_k).
 * Cross-attention with one fused W_QKV: Q = X_q W_QKV[:, :D] + b[:D] and
   [K | V] = X_kv W_QKV[:, D:] + b[D:].
+* Grouped key/value heads (n_g = n_kv_heads sets, n_g divides h): the fused
+  matrix is (D, D + 2 n_g d_k) with column blocks [Q | K | V], set g owning
+  columns [g*d_k, (g+1)*d_k) of the K and of the V block, and query head i
+  uses set i // (h / n_g) (consecutive query heads form a group). n_g = h is
+  plain multi-head attention, n_g = 1 multi-query attention.
 * The scale is 1/sqrt(d_k) (one page prints QK^T/d_k; every other statement,
   including the variance argument of §8 on iamjaehka13.blog, has the root).
 * softmax subtracts the row maximum before exponentiating. In exact
@@ -105,25 +115,50 @@ def _as64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
 
+def kv_head_of(h: int, n_kv_heads: int) -> np.ndarray:
+    """Key/value set used by each query head: head i -> i // (h / n_g)."""
+    if n_kv_heads < 1 or h % n_kv_heads != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    return np.arange(h) // (h // n_kv_heads)
+
+
 def _qkv(x_q, x_kv, w_qkv, b_qkv, D):
-    """Fused projection: one D x 3D matrix for self-attention; for
-    cross-attention Q comes from x_q and K, V from x_kv."""
+    """Fused projection: one D x (D + 2 D_kv) matrix for self-attention; for
+    cross-attention Q comes from x_q and K, V from x_kv. D_kv = n_g d_k
+    (= D for plain multi-head attention)."""
+    d_kv = (w_qkv.shape[1] - D) // 2
     if x_kv is None:
         y = linear(x_q, w_qkv, b_qkv)
-        return y[..., :D], y[..., D:2 * D], y[..., 2 * D:]
+        return y[..., :D], y[..., D:D + d_kv], y[..., D + d_kv:]
     bq = None if b_qkv is None else b_qkv[:D]
     bkv = None if b_qkv is None else b_qkv[D:]
     q = linear(x_q, w_qkv[:, :D], bq)
     kv = linear(x_kv, w_qkv[:, D:], bkv)
-    return q, kv[..., :D], kv[..., D:]
+    return q, kv[..., :d_kv], kv[..., d_kv:]
+
+
+def _kv_width(w_qkv, D, h, n_kv_heads):
+    n_g = h if n_kv_heads is None else n_kv_heads
+    kv_head_of(h, n_g)
+    if w_qkv.shape[1] != D + 2 * n_g * (D // h):
+        raise ValueError("W_QKV must be (D, D + 2 n_kv_heads d_k)")
+    return n_g
+
+
+def _attend_grouped(qh, kh, vh, n_g, causal, mask, q_pos=None):
+    """Attention with key/value set kv_head_of(h, n_g)[i] for query head i."""
+    h = qh.shape[1]
+    sel = kv_head_of(h, n_g)
+    return attention(qh, kh[:, sel], vh[:, sel], causal, mask, q_pos)
 
 
 def mha_forward(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
-                key_padding_mask=None, return_intermediates=False):
+                key_padding_mask=None, return_intermediates=False, n_kv_heads=None):
     """Y = Concat(head_1..head_h) W^O + b_O for batch-first inputs.
 
     x_q (B, T_q, D); x_kv (B, T_k, D) or None for self-attention;
-    w_qkv (D, 3D); b_qkv (3D,) or None; w_o (D, D); b_o (D,) or None;
+    w_qkv (D, D + 2 n_g d_k) (3D wide for n_kv_heads None = h);
+    b_qkv (D + 2 n_g d_k,) or None; w_o (D, D); b_o (D,) or None;
     key_padding_mask (B, T_k), nonzero = ignore, or None.
     Everything is evaluated in float64.
     """
@@ -133,9 +168,11 @@ def mha_forward(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
         raise ValueError("embed_dim must be divisible by num_heads")
     if causal and x_kv is not None and x_kv.shape[1] != T_q:
         raise ValueError("causal mask needs T_q == T_k")
+    n_g = _kv_width(w_qkv, D, h, n_kv_heads)
     q, k, v = _qkv(x_q, x_kv, w_qkv, b_qkv, D)
-    qh, kh, vh = (split_heads(t, h) for t in (q, k, v))
-    o, a = attention(qh, kh, vh, causal, key_padding_mask)
+    qh = split_heads(q, h)
+    kh, vh = split_heads(k, n_g), split_heads(v, n_g)
+    o, a = _attend_grouped(qh, kh, vh, n_g, causal, key_padding_mask)
     o_cat = concat_heads(o)
     y = linear(o_cat, w_o, b_o)
     if return_intermediates:
@@ -144,7 +181,7 @@ def mha_forward(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
 
 
 def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
-                     causal=False, key_padding_mask=None):
+                     causal=False, key_padding_mask=None, n_kv_heads=None):
     """Y[b, t, :] for selected query rows only.
 
     ``rows`` maps a batch index b to a 1-D array of query positions t. The
@@ -155,6 +192,8 @@ def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
     """
     w_qkv, b_qkv, w_o, b_o = map(_as64, (w_qkv, b_qkv, w_o, b_o))
     D = w_qkv.shape[0]
+    n_g = _kv_width(w_qkv, D, h, n_kv_heads)
+    d_kv = n_g * (D // h)
     out = {}
     for b, ts in rows.items():
         ts = np.asarray(ts, dtype=np.int64)
@@ -164,20 +203,32 @@ def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
         bkv = None if b_qkv is None else b_qkv[D:]
         q = linear(xq_b, w_qkv[:, :D], bq)
         kv = linear(xkv_b, w_qkv[:, D:], bkv)
-        k, v = kv[..., :D], kv[..., D:]
+        k, v = kv[..., :d_kv], kv[..., d_kv:]
         mask_b = None if key_padding_mask is None else np.asarray(key_padding_mask)[b:b + 1]
-        qh, kh, vh = (split_heads(t, h) for t in (q, k, v))
-        o, _ = attention(qh, kh, vh, causal, mask_b, q_pos=ts)
+        qh = split_heads(q, h)
+        kh, vh = split_heads(k, n_g), split_heads(v, n_g)
+        o, _ = _attend_grouped(qh, kh, vh, n_g, causal, mask_b, q_pos=ts)
         out[b] = linear(concat_heads(o), w_o, b_o)[0]
     return out
 
 
-def param_count(D: int, h: int, bias: bool = True) -> int:
+def param_count(D: int, h: int, bias: bool = True, n_kv_heads=None) -> int:
     """Number of parameters of one MHA layer as this module stores them:
-    W_QKV (D x 3D), W_O (D x D) and, with ``bias``, b_QKV (3D) and b_O (D).
-    The head count only slices the same matrices (molayo1419.me, parameter
-    table: 4E^2 + 4E for every num_heads)."""
+    W_QKV (D x (D + 2 n_g d_k)), W_O (D x D) and, with ``bias``, b_QKV and
+    b_O. With n_g = h the head count only slices the same matrices
+    (molayo1419.me, parameter table: 4E^2 + 4E for every num_heads)."""
     if D % h != 0:
         raise ValueError("embed_dim must be divisible by num_heads")
-    shapes = [(D, 3 * D), (D, D)] + ([(3 * D,), (D,)] if bias else [])
+    n_g = h if n_kv_heads is None else n_kv_heads
+    kv_head_of(h, n_g)
+    n_qkv = D + 2 * n_g * (D // h)
+    shapes = [(D, n_qkv), (D, D)] + ([(n_qkv,), (D,)] if bias else [])
     return int(sum(np.prod(s) for s in shapes))
+
+
+def kv_elements_per_token(D: int, h: int, n_kv_heads=None) -> int:
+    """Key and value elements one token leaves per layer: the widths of the
+    K and V blocks of the projection output."""
+    n_g = h if n_kv_heads is None else n_kv_heads
+    kv_head_of(h, n_g)
+    return 2 * n_g * (D // h)
