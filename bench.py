@@ -57,7 +57,7 @@ def stage_flops(w, stage: str) -> float:
         f = 4.0 * w.T_q * w.T_k * D * w.B
         return f * 0.5 if w.causal else f
     if stage == "qkv_proj":
-        return 2.0 * w.B * (w.T_q * D * D + w.T_k * D * 2 * D)
+        return 2.0 * w.B * (w.T_q * D * D + w.T_k * D * 2 * w.n_g * w.d_k)
     if stage == "out_proj":
         return 2.0 * w.B * w.T_q * D * D
     return 0.0
@@ -99,7 +99,7 @@ def cpu_baseline(w, inp, budget_s: float = 10.0):
         mha_oracle.mha_forward(
             f(inp["x_q"][b]), wq, bq, wo, bo, w.h,
             x_kv=None if inp["x_kv"] is None else f(inp["x_kv"][b]), causal=w.causal,
-            key_padding_mask=None if mask is None else mask[b].numpy())
+            key_padding_mask=None if mask is None else mask[b].numpy(), n_kv_heads=w.n_g)
         spent += time.perf_counter() - t0
         done += 1
     flops = w.flops() / w.B * done
@@ -144,14 +144,14 @@ def main() -> int:
     if args.copy_calibration:
         return copy_calibration(torch, args.steps)
     import transformer_head_attention_amd as mha
-    from mha_inputs import WORKLOADS, HEADLINE, make_inputs
+    from mha_inputs import ALL_WORKLOADS, HEADLINE, make_inputs
 
     name = args.workload or HEADLINE
-    w = WORKLOADS[name]
+    w = ALL_WORKLOADS[name]
     inp = make_inputs(w, seed=0)
     dev = torch.device("cuda:0")
     t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
-    m = mha.MultiHeadAttention(w.D, w.h, w.dtype)
+    m = mha.MultiHeadAttention(w.D, w.h, w.dtype, num_kv_heads=w.n_g)
     ws = m.workspace(w.B, w.T_q, w.T_k, dev)
     y = torch.empty(w.B, w.T_q, w.D, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -208,7 +208,7 @@ def main() -> int:
         "dtype": "bf16" if w.dtype == "bf16" else "fp32",
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "T_q": w.T_q, "T_k": w.T_k, "D": w.D, "h": w.h,
-                   "d_k": w.d_k, "causal": w.causal, "cross": w.cross,
+                   "n_kv_heads": w.n_g, "d_k": w.d_k, "causal": w.causal, "cross": w.cross,
                    "key_padding": w.padding is not None, "gflop_per_step": round(flops / 1e9, 3),
                    "intermediates": "fp16 Q/K/V/P/O, fp32 accumulate, fp32 Y"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_MFMA_16BIT_TFLOPS, 2),

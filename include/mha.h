@@ -16,15 +16,22 @@
  *     §19 (cross-attention: Q from the target, K and V from the source).
  *   molayo1419.me "MHA란 무엇인가?", trap 2 (key_padding_mask: nonzero/True
  *     means IGNORE the key) and trap 3 (every key ignored -> 0/0 -> NaN).
+ *   itwiki "멀티 헤드 어텐션", section 추론 비용과 변형 (variants table):
+ *     grouped key/value heads -- h query heads share n_g key/value sets
+ *     (GQA; n_g = 1 is MQA, n_g = h plain multi-head attention).
  *
  * Conventions:
  *   - Batch-first only: every activation is (B, T, D) row-major.
- *   - Weights multiply from the right, y = x . W + b. W_QKV is (D, 3D)
- *     row-major with column blocks [Q | K | V]; head i owns columns
- *     [i*d_k, (i+1)*d_k) inside each block. W_O is (D, D) row-major.
- *     (torch.nn.Linear / nn.MultiheadAttention store the transpose.)
+ *   - Weights multiply from the right, y = x . W + b. W_QKV is (D, N_qkv)
+ *     row-major, N_qkv = D + 2 * n_g * d_k (= 3D when n_g = h), with column
+ *     blocks [Q (D wide) | K (n_g*d_k) | V (n_g*d_k)]; query head i owns
+ *     columns [i*d_k, (i+1)*d_k) of the Q block, key/value set g owns
+ *     columns [g*d_k, (g+1)*d_k) of the K and of the V block, and query head
+ *     i reads set i / (h / n_g) (consecutive query heads form a group).
+ *     W_O is (D, D) row-major. (torch.nn.Linear / nn.MultiheadAttention
+ *     store the transpose.)
  *   - Cross-attention (x_kv != NULL): Q = x_q W_QKV[:, 0:D] + b_QKV[0:D],
- *     [K | V] = x_kv W_QKV[:, D:3D] + b_QKV[D:3D].
+ *     [K | V] = x_kv W_QKV[:, D:N_qkv] + b_QKV[D:N_qkv].
  *   - KEY PADDING MASK: NONZERO = THIS KEY IS IGNORED (nn.MultiheadAttention's
  *     key_padding_mask convention, NOT the SDPA boolean attn_mask convention).
  *   - causal = 1 masks keys j > i (requires T_q == T_k). It is a real mask,
@@ -49,8 +56,9 @@
  *     workspaces differ and no profiling is active.
  *
  * Supported on the GPU: d_k = D / h in {64, 128}, D a multiple of 128,
- * B, T_q, T_k >= 1. fp16 overflow bound: every projected Q, K, V value and
- * every attention output must stay below 65504 in magnitude (bf16 path).
+ * n_g dividing h, B, T_q, T_k >= 1. fp16 overflow bound: every projected
+ * Q, K, V value and every attention output must stay below 65504 in
+ * magnitude (bf16 path).
  */
 #ifndef MHA_H
 #define MHA_H
@@ -79,6 +87,14 @@ typedef enum {
  * MHA_ERR_UNSUPPORTED. On error *out is set to NULL. */
 mha_status_t mha_create(mha_handle_t* out, int d_model, int num_heads, mha_dtype_t dtype);
 
+/* As mha_create, with num_kv_heads = n_g key/value sets shared by groups of
+ * num_heads / n_g consecutive query heads (itwiki "멀티 헤드 어텐션",
+ * 추론 비용과 변형: GQA, and MQA for n_g = 1). W_QKV and b_QKV are then
+ * D + 2 * n_g * d_k wide. num_kv_heads < 1 or not dividing num_heads ->
+ * MHA_ERR_INVALID_ARG. mha_create(.., h, ..) equals num_kv_heads = h. */
+mha_status_t mha_create_grouped(mha_handle_t* out, int d_model, int num_heads, int num_kv_heads,
+                                mha_dtype_t dtype);
+
 /* Bytes of device workspace mha_forward needs for these sizes (0 if the
  * handle or sizes are invalid). Pass T_k = T_q for self-attention. */
 size_t mha_workspace_size(mha_handle_t handle, int B, int T_q, int T_k);
@@ -87,8 +103,8 @@ size_t mha_workspace_size(mha_handle_t handle, int B, int T_q, int T_k);
  *   x_q   (B, T_q, D)  dtype   queries (and keys/values if x_kv == NULL)
  *   x_kv  (B, T_k, D)  dtype   keys/values source, or NULL for self-attention
  *                              (then T_k must equal T_q)
- *   w_qkv (D, 3D)      dtype   row-major, y = x . W
- *   b_qkv (3D)         dtype   or NULL (zero bias)
+ *   w_qkv (D, N_qkv)   dtype   row-major, y = x . W; N_qkv = D + 2 n_g d_k
+ *   b_qkv (N_qkv)      dtype   or NULL (zero bias)
  *   w_o   (D, D)       dtype   row-major
  *   b_o   (D)          dtype   or NULL (zero bias)
  *   causal             0 or 1

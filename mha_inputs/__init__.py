@@ -16,12 +16,15 @@ Workloads follow the pages' own settings where they give them:
   "[Deep Learning 5] Attention의 내부 계산", §19).
 * A key-padding mask marks keys to IGNORE with a nonzero value, the
   nn.MultiheadAttention convention described in molayo1419.me, trap 2.
+* Grouped key/value heads (itwiki, 추론 비용과 변형, variants table): n_g
+  key/value sets for n_h query heads; W_QKV is then (D, D + 2 n_g d_k).
 
 Readings taken where the workload text is silent (each is listed in the
 design notes):
 
 * "Xavier-uniform" is U(-a, a), a = sqrt(6 / (fan_in + fan_out)), gain 1.
-  For the fused (D, 3D) projection fan_in = D, fan_out = 3D.
+  For the fused (D, 3D) projection fan_in = D, fan_out = 3D (D + 2 n_g d_k
+  with grouped key/value heads).
 * "N(0, s)" names the standard deviation s.
 * Key padding is trailing: keys j >= len_b of batch element b are masked,
   with len_b an integer drawn uniformly from [256, 2048] inclusive.
@@ -59,16 +62,28 @@ class Workload:
     weight_init: str = "xavier"       # "xavier" or ("normal", std)
     weight_std: float = 0.0
     bias_std: Optional[float] = None  # None -> zero biases
+    n_kv: Optional[int] = None        # key/value sets n_g (None -> h, plain MHA)
 
     @property
     def d_k(self) -> int:
         return self.D // self.h
 
+    @property
+    def n_g(self) -> int:
+        return self.h if self.n_kv is None else self.n_kv
+
+    @property
+    def n_qkv(self) -> int:
+        """Width of the fused projection: D + 2 n_g d_k."""
+        return self.D + 2 * self.n_g * self.d_k
+
     def flops(self) -> float:
         """Formula FLOPs: projections 4*T_q*D^2 + 4*T_k*D^2 (8*T*D^2 when
         T_q == T_k) plus 4*T_q*T_k*D for scores and weighted sum, halved
-        under a causal mask, per batch element (itwiki, 매개변수와 계산량)."""
-        proj = 4.0 * self.T_q * self.D ** 2 + 4.0 * self.T_k * self.D ** 2
+        under a causal mask, per batch element (itwiki, 매개변수와 계산량).
+        With n_g key/value sets the K and V projections are n_g d_k wide:
+        4*T_k*D*n_g*d_k instead of 4*T_k*D^2."""
+        proj = 4.0 * self.T_q * self.D ** 2 + 4.0 * self.T_k * self.D * self.n_g * self.d_k
         attn = 4.0 * self.T_q * self.T_k * self.D
         if self.causal:
             attn *= 0.5
@@ -94,6 +109,19 @@ WORKLOADS = {
                  causal=True, weight_init="normal", weight_std=1.0 / 64.0),
     ]
 }
+
+# Grouped key/value heads at the d_model = 1024 causal shape: GQA with 4 sets
+# of 4 query heads, and MQA (one set shared by all 16 heads).
+GROUPED_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("gqa4_causal_bf16_d1024_h16_b8_t4096", "bf16", 1024, 16, 8, 4096, 4096,
+                 causal=True, bias_std=0.02, n_kv=4),
+        Workload("mqa_causal_bf16_d1024_h16_b8_t4096", "bf16", 1024, 16, 8, 4096, 4096,
+                 causal=True, bias_std=0.02, n_kv=1),
+    ]
+}
+ALL_WORKLOADS = {**WORKLOADS, **GROUPED_WORKLOADS}
 
 HEADLINE = "causal_bf16_d1024_h16_b8_t4096"
 
@@ -124,17 +152,18 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     D = w.D
     x_q = _normal(g, (w.B, w.T_q, D), 1.0)
     x_kv = _normal(g, (w.B, w.T_k, D), 1.0) if w.cross else None
+    n_qkv = w.n_qkv
     if w.weight_init == "xavier":
-        w_qkv = _uniform(g, (D, 3 * D), math.sqrt(6.0 / (D + 3 * D)))
+        w_qkv = _uniform(g, (D, n_qkv), math.sqrt(6.0 / (D + n_qkv)))
         w_o = _uniform(g, (D, D), math.sqrt(6.0 / (D + D)))
     else:
-        w_qkv = _normal(g, (D, 3 * D), w.weight_std)
+        w_qkv = _normal(g, (D, n_qkv), w.weight_std)
         w_o = _normal(g, (D, D), w.weight_std)
     if w.bias_std is None:
-        b_qkv = torch.zeros(3 * D)
+        b_qkv = torch.zeros(n_qkv)
         b_o = torch.zeros(D)
     else:
-        b_qkv = _normal(g, (3 * D,), w.bias_std)
+        b_qkv = _normal(g, (n_qkv,), w.bias_std)
         b_o = _normal(g, (D,), w.bias_std)
     mask = None
     lengths = None
@@ -154,6 +183,7 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         "key_padding_mask": mask,
         "lengths": lengths,
         "h": w.h,
+        "n_kv": w.n_g,
         "causal": w.causal,
     }
     return out

@@ -125,3 +125,29 @@ def test_profile_calls_validate(mha):
         assert mha.mha_profile_begin(None, 4) == mha.MHA_ERR_INVALID_ARG
     finally:
         mha.mha_destroy(h)
+
+
+def test_create_grouped_validation_and_workspace(mha):
+    for n_g in (0, -1, 3, 5, 32):                          # < 1 or not dividing 16
+        st, h = mha.mha_create_grouped(1024, 16, n_g, mha.MHA_BF16)
+        assert st == mha.MHA_ERR_INVALID_ARG and h is None
+    st, h = mha.mha_create_grouped(256, 8, 2, mha.MHA_BF16)   # d_k = 32
+    assert st == mha.MHA_ERR_UNSUPPORTED
+    sizes = {}
+    for n_g in (16, 4, 1):
+        st, h = mha.mha_create_grouped(1024, 16, n_g, mha.MHA_BF16)
+        assert st == mha.MHA_OK and h
+        sizes[n_g] = mha.mha_workspace_size(h, 8, 4096, 4096)
+        mha.mha_destroy(h)
+    st, h = mha.mha_create(1024, 16, mha.MHA_BF16)
+    assert mha.mha_workspace_size(h, 8, 4096, 4096) == sizes[16]
+    mha.mha_destroy(h)
+    # K and V^T shrink by n_g / h: two (B, T, D) fp16 buffers scaled down
+    full_kv = 2 * 8 * 4096 * 1024 * 2
+    assert sizes[16] - sizes[4] >= full_kv * 3 // 4 - 4096
+    assert sizes[4] > sizes[1] > 0
+    for dt in (mha.MHA_F32, mha.MHA_BF16):
+        st, h = mha.mha_create_grouped(512, 8, 2, dt)
+        assert st == mha.MHA_OK
+        assert mha.mha_workspace_size(h, 2, 100, 300) > 0
+        mha.mha_destroy(h)

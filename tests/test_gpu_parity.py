@@ -6,7 +6,9 @@ NaN positions (rows whose keys are all masked) must match exactly.
 
 * Mid-size cases compare every output element; their sizes span several
   tiles and end in ragged tails.
-* The five full-size workloads run exactly as the benchmark launches them;
+* Grouped key/value heads (GQA, MQA): the same mid-size shapes with n_g < h
+  sets, plus two full-size grouped workloads.
+* The full-size workloads run exactly as the benchmark launches them;
   the oracle evaluates sampled rows (all early causal rows of two batch
   elements, the last rows, and uniformly drawn rows whose RMS normalises the
   error).
@@ -19,7 +21,7 @@ import numpy as np
 import pytest
 import torch
 
-from mha_inputs import WORKLOADS, make_inputs, as_float64_numpy
+from mha_inputs import ALL_WORKLOADS, WORKLOADS, make_inputs, as_float64_numpy
 from oracle import mha_oracle as mo
 
 pytestmark = pytest.mark.gpu
@@ -43,7 +45,7 @@ def _dev(t):
 
 
 def run_gpu(lib, w, inp, stream=None, none_bias=False, mod=None):
-    m = mod or lib.MultiHeadAttention(w.D, w.h, w.dtype)
+    m = mod or lib.MultiHeadAttention(w.D, w.h, w.dtype, num_kv_heads=w.n_g)
     y = m.forward(_dev(inp["x_q"]), _dev(inp["w_qkv"]), _dev(inp["w_o"]),
                   b_qkv=None if none_bias else _dev(inp["b_qkv"]),
                   b_o=None if none_bias else _dev(inp["b_o"]),
@@ -62,14 +64,15 @@ def oracle_full(inp):
     f = as_float64_numpy
     return mo.mha_forward(f(inp["x_q"]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]),
                           f(inp["b_o"]), inp["h"], x_kv=f(inp["x_kv"]), causal=inp["causal"],
-                          key_padding_mask=_np_mask(inp))
+                          key_padding_mask=_np_mask(inp), n_kv_heads=inp["n_kv"])
 
 
 def oracle_rows(inp, rows):
     f = as_float64_numpy
     return mo.mha_forward_rows(f(inp["x_q"]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]),
                                f(inp["b_o"]), inp["h"], rows, x_kv=f(inp["x_kv"]),
-                               causal=inp["causal"], key_padding_mask=_np_mask(inp))
+                               causal=inp["causal"], key_padding_mask=_np_mask(inp),
+                               n_kv_heads=inp["n_kv"])
 
 
 def rel_err(y, ref, rms=None):
@@ -108,6 +111,30 @@ MID = [
     ("bf16 T=65 causal", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=2, T_q=65, T_k=65)),
     ("bf16 T=129 causal d_k=128", W["causal_bf16_d4096_h32_b1_t8192"], dict(D=1024, h=8,
                                                                               T_q=129, T_k=129)),
+    # grouped key/value heads
+    ("bf16 GQA g4 causal d1024 ragged", W["causal_bf16_d1024_h16_b8_t4096"],
+     dict(B=1, T_q=777, T_k=777, n_kv=4)),
+    ("bf16 GQA g8 non-causal d1024", W["causal_bf16_d1024_h16_b8_t4096"],
+     dict(B=2, T_q=257, T_k=257, causal=False, n_kv=8)),
+    ("bf16 MQA causal d512 (64-wide K, V blocks)", W["causal_bf16_d512_h8_b16_t1024"],
+     dict(B=2, T_q=300, T_k=300, n_kv=1)),
+    ("bf16 MQA causal + padding d512", W["causal_bf16_d512_h8_b16_t1024"],
+     dict(B=3, T_q=190, T_k=190, padding=(150, 190), n_kv=1)),
+    ("bf16 GQA g2 cross padded ragged", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
+     dict(B=3, T_q=200, T_k=333, padding=(40, 333), n_kv=2)),
+    ("bf16 MQA cross padded ragged", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
+     dict(B=2, T_q=77, T_k=201, padding=(40, 201), n_kv=1)),
+    ("bf16 GQA g2 causal d_k=128", W["causal_bf16_d4096_h32_b1_t8192"],
+     dict(D=1024, h=8, T_q=300, T_k=300, n_kv=2)),
+    ("bf16 MQA causal d_k=128 T=129", W["causal_bf16_d4096_h32_b1_t8192"],
+     dict(D=1024, h=8, T_q=129, T_k=129, n_kv=1)),
+    ("bf16 GQA T=1 causal", W["causal_bf16_d512_h8_b16_t1024"], dict(B=3, T_q=1, T_k=1, n_kv=2)),
+    ("fp32 GQA g2 causal ragged", W["self_fp32_d512_h8_b2_t128"],
+     dict(T_q=201, T_k=201, causal=True, n_kv=2)),
+    ("fp32 MQA cross padded", W["self_fp32_d512_h8_b2_t128"],
+     dict(B=3, T_q=77, T_k=150, cross=True, padding=(1, 150), n_kv=1)),
+    ("fp32 GQA g4 d_k=128", W["self_fp32_d512_h8_b2_t128"],
+     dict(D=1024, h=8, T_q=99, T_k=99, causal=True, n_kv=4)),
 ]
 
 
@@ -186,9 +213,9 @@ def _sample_rows(w, rng):
     return bs, uni, extra
 
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("name", list(ALL_WORKLOADS))
 def test_full_size_workload(lib, name):
-    w = WORKLOADS[name]
+    w = ALL_WORKLOADS[name]
     _say(f"[parity] full size {name}")
     inp = make_inputs(w, seed=0)
     y = run_gpu(lib, w, inp)
@@ -205,3 +232,14 @@ def test_full_size_workload(lib, name):
     _say(f"[parity] full size {name}: err/rms = {err:.3e} (tol {TOL[w.dtype]})")
     assert np.isfinite(y).all()
     assert err <= TOL[w.dtype]
+
+
+def test_grouped_with_one_set_per_head_equals_plain(lib):
+    """num_kv_heads = num_heads runs the same kernels as mha_create: bitwise
+    equal results."""
+    w = W["causal_bf16_d512_h8_b16_t1024"].shrink(B=2, T_q=200, T_k=200, bias_std=0.02)
+    _say(f"[parity] grouped handle with n_g = h vs plain handle: {w}")
+    inp = make_inputs(w, seed=9)
+    plain = lib.MultiHeadAttention(w.D, w.h, "bf16")
+    grouped = lib.MultiHeadAttention(w.D, w.h, "bf16", num_kv_heads=w.h)
+    assert np.array_equal(run_gpu(lib, w, inp, mod=plain), run_gpu(lib, w, inp, mod=grouped))

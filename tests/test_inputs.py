@@ -5,7 +5,7 @@ import math
 
 import torch
 
-from mha_inputs import WORKLOADS, HEADLINE, make_inputs
+from mha_inputs import ALL_WORKLOADS, GROUPED_WORKLOADS, WORKLOADS, HEADLINE, make_inputs
 
 
 def _digest(inp):
@@ -26,13 +26,15 @@ def test_deterministic_per_seed_and_distinct_across_seeds():
 
 
 def test_shapes_and_dtypes_of_every_workload():
-    for name, w in WORKLOADS.items():
+    for name, w in ALL_WORKLOADS.items():
         small = w.shrink(B=min(w.B, 2), T_q=min(w.T_q, 64), T_k=min(w.T_k, 64),
                          padding=None if w.padding is None else (8, 64))
         inp = make_inputs(small, 0)
         dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
         assert inp["x_q"].shape == (small.B, small.T_q, w.D) and inp["x_q"].dtype == dt
-        assert inp["w_qkv"].shape == (w.D, 3 * w.D) and inp["w_o"].shape == (w.D, w.D)
+        n_qkv = w.D + 2 * (w.h if w.n_kv is None else w.n_kv) * (w.D // w.h)
+        assert inp["w_qkv"].shape == (w.D, n_qkv) and inp["b_qkv"].shape == (n_qkv,)
+        assert inp["w_o"].shape == (w.D, w.D)
         assert (inp["x_kv"] is not None) == w.cross
         assert (inp["key_padding_mask"] is not None) == (w.padding is not None)
         if w.bias_std is None:
@@ -68,3 +70,18 @@ def test_padding_mask_is_trailing_with_lengths_in_range():
 def test_flop_formula_headline():
     w = WORKLOADS[HEADLINE]
     assert abs(w.flops() / 1e9 - 549.7558) < 1e-3
+
+
+def test_grouped_workloads_shapes_and_flops():
+    gqa = GROUPED_WORKLOADS["gqa4_causal_bf16_d1024_h16_b8_t4096"]
+    mqa = GROUPED_WORKLOADS["mqa_causal_bf16_d1024_h16_b8_t4096"]
+    assert (gqa.n_g, gqa.n_qkv) == (4, 1024 + 2 * 4 * 64)
+    assert (mqa.n_g, mqa.n_qkv) == (1, 1024 + 2 * 64)
+    # Q and output projections 4TD^2, K and V 4TD n_g d_k, attention 2T^2D (causal)
+    T, D, B = 4096, 1024, 8
+    for w in (gqa, mqa):
+        expect = B * (4 * T * D * D + 4 * T * D * w.n_g * 64 + 2 * T * T * D)
+        assert abs(w.flops() - expect) < 1
+    # plain MHA draws are unchanged by the grouped-head field
+    small = WORKLOADS[HEADLINE].shrink(B=1, T_q=8, T_k=8)
+    assert make_inputs(small, 0)["w_qkv"].shape == (1024, 3072)

@@ -33,13 +33,15 @@ MHA_F32, MHA_BF16 = 0, 1
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP = range(5)
 MHA_NUM_STAGES = 5
 
-EXPORTED = ("mha_create", "mha_workspace_size", "mha_forward", "mha_destroy",
+EXPORTED = ("mha_create", "mha_create_grouped", "mha_workspace_size", "mha_forward", "mha_destroy",
             "mha_status_string", "mha_hip_error_string", "mha_profile_begin", "mha_profile_end",
             "mha_stage_name")
 
 _vp, _int, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _lib.mha_create.argtypes = [ctypes.POINTER(_vp), _int, _int, _int]
 _lib.mha_create.restype = _int
+_lib.mha_create_grouped.argtypes = [ctypes.POINTER(_vp), _int, _int, _int, _int]
+_lib.mha_create_grouped.restype = _int
 _lib.mha_workspace_size.argtypes = [_vp, _int, _int, _int]
 _lib.mha_workspace_size.restype = _sz
 _lib.mha_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
@@ -95,6 +97,14 @@ def mha_create(d_model: int, num_heads: int, dtype: int):
     return st, (h.value if st == MHA_OK else None)
 
 
+def mha_create_grouped(d_model: int, num_heads: int, num_kv_heads: int, dtype: int):
+    """Returns (status, handle); handle is None on error."""
+    h = _vp()
+    st = _lib.mha_create_grouped(ctypes.byref(h), int(d_model), int(num_heads),
+                                 int(num_kv_heads), int(dtype))
+    return st, (h.value if st == MHA_OK else None)
+
+
 def mha_workspace_size(handle, B: int, T_q: int, T_k: int) -> int:
     return int(_lib.mha_workspace_size(handle, int(B), int(T_q), int(T_k)))
 
@@ -130,16 +140,21 @@ class MultiHeadAttention:
     ``mha_forward`` on torch CUDA tensors.
 
     dtype is "bf16" (bf16 inputs/weights, fp32 output) or "fp32".
+    num_kv_heads (default num_heads) selects grouped key/value heads; W_QKV
+    is then (d_model, d_model + 2 * num_kv_heads * d_k).
     """
 
-    def __init__(self, d_model: int, num_heads: int, dtype: str = "bf16"):
+    def __init__(self, d_model: int, num_heads: int, dtype: str = "bf16",
+                 num_kv_heads: int = None):
         import torch
         self._torch = torch
         self.d_model, self.num_heads = d_model, num_heads
+        self.num_kv_heads = num_heads if num_kv_heads is None else num_kv_heads
         self.dtype = dtype
         self._tdtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
-        st, h = mha_create(d_model, num_heads, MHA_BF16 if dtype == "bf16" else MHA_F32)
-        _check(st, "mha_create")
+        st, h = mha_create_grouped(d_model, num_heads, self.num_kv_heads,
+                                   MHA_BF16 if dtype == "bf16" else MHA_F32)
+        _check(st, "mha_create_grouped")
         self.handle = h
         self._ws = None
 
@@ -174,9 +189,24 @@ class MultiHeadAttention:
             raise TypeError(f"expected {dtype}, got {t.dtype}")
         return t.data_ptr()
 
+    def _check_shapes(self, x_q, w_qkv, w_o, b_qkv, b_o, x_kv, key_padding_mask, out):
+        D = self.d_model
+        n_qkv = D + 2 * self.num_kv_heads * (D // self.num_heads)
+        B, T_q = x_q.shape[0], x_q.shape[1]
+        T_k = T_q if x_kv is None else x_kv.shape[1]
+        want = [(x_q, (B, T_q, D)), (w_qkv, (D, n_qkv)), (w_o, (D, D)), (b_qkv, (n_qkv,)),
+                (b_o, (D,)), (x_kv, (B, T_k, D)), (key_padding_mask, (B, T_k)),
+                (out, (B, T_q, D))]
+        for t, shape in want:
+            if t is not None and tuple(t.shape) != shape:
+                raise ValueError(f"expected shape {shape}, got {tuple(t.shape)}")
+
     def forward(self, x_q, w_qkv, w_o, b_qkv=None, b_o=None, x_kv=None, causal=False,
                 key_padding_mask=None, out=None, workspace=None, stream=None):
         torch = self._torch
+        if x_q.dim() != 3:
+            raise ValueError("x_q must be (B, T, D)")
+        self._check_shapes(x_q, w_qkv, w_o, b_qkv, b_o, x_kv, key_padding_mask, out)
         B, T_q, D = x_q.shape
         T_k = T_q if x_kv is None else x_kv.shape[1]
         if out is None:

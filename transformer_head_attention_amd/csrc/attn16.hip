@@ -107,10 +107,14 @@ attn_f16_kernel(AttnF16Args a) {
   int qblk = logical - bh * nqb;
   if (a.causal) qblk = nqb - 1 - qblk;
   const int b = bh / a.h, head = bh - b * a.h;
+  // Key/value set of this query head: consecutive heads share one set, and
+  // their workgroups are consecutive in the XCD mapping above, so a set's K
+  // and V are read into one XCD's L2 for the whole group.
+  const int kvh = b * a.h_kv + head / (a.h / a.h_kv);
 
   const uint16_t* Qg = a.q + (size_t)bh * a.Tqp * DK;
-  const uint16_t* Kg = a.k + (size_t)bh * a.Tkp * DK;
-  const uint16_t* Vg = a.vt + (size_t)bh * DK * a.Tkp;
+  const uint16_t* Kg = a.k + (size_t)kvh * a.Tkp * DK;
+  const uint16_t* Vg = a.vt + (size_t)kvh * DK * a.Tkp;
   const int qw0 = qblk * BLOCK_M + wave * 32 * NQ;
 
   int kv_end = a.T_k;
@@ -410,6 +414,7 @@ hipError_t launch_mask_bits(const uint8_t* mask, int B, int T_k, uint32_t* bits,
 }
 
 hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, hipStream_t s) {
+  if (a.h_kv < 1 || a.h % a.h_kv != 0) return hipErrorInvalidValue;
   const int bm = attn_f16_block_m(d_k);
   const int total = (a.Tqp / bm) * a.h * a.B;
   if (d_k == 64) return launch_dk<64, MHA_ATTN_NS64>(a, total, s);

@@ -130,8 +130,8 @@ attn_f32_kernel(AttnF32Args a) {
 
   int kend = a.T_k;
   if (a.causal) kend = min(kend, blockIdx.x * RPB + RPB);
-  const float* kb = a.k + (size_t)b * a.kv_bstride + head * DK;
-  const float* vb = a.v + (size_t)b * a.kv_bstride + head * DK;
+  const float* kb = a.k + (size_t)b * a.kv_bstride + (head / a.group) * DK;
+  const float* vb = a.v + (size_t)b * a.kv_bstride + (head / a.group) * DK;
   const uint8_t* mb = a.mask ? a.mask + (size_t)b * a.mask_ld : nullptr;
 
   for (int j0 = 0; j0 < kend; j0 += KC) {
@@ -219,8 +219,8 @@ attn_early_kernel(AttnF32Args a) {
   // Keys [0, kend) of this head; rows past kend are zero so that the key
   // loops below can run over all 64 rows without branches (their weights
   // are exactly 0 and 0 * 0 stays 0).
-  const float* kb = a.k + (size_t)b * a.kv_bstride + head * DK;
-  const float* vb = a.v + (size_t)b * a.kv_bstride + head * DK;
+  const float* kb = a.k + (size_t)b * a.kv_bstride + (head / a.group) * DK;
+  const float* vb = a.v + (size_t)b * a.kv_bstride + (head / a.group) * DK;
   for (int idx = tid; idx < 64 * (DK / 4); idx += 256) {
     const int key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
     f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
@@ -300,6 +300,7 @@ hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B,
 
 hipError_t launch_attn_early(const AttnF32Args& a, int d_k, hipStream_t s) {
   if (a.T_k < 1 || a.T_k > 64 || a.rows > a.T_k) return hipErrorInvalidValue;
+  if (a.group < 1 || a.h % a.group != 0) return hipErrorInvalidValue;
   dim3 grid((a.rows + ER - 1) / ER, a.h, a.B);
   if (d_k == 64)
     hipLaunchKernelGGL(attn_early_kernel<64>, grid, dim3(256), 0, s, a);
@@ -311,6 +312,7 @@ hipError_t launch_attn_early(const AttnF32Args& a, int d_k, hipStream_t s) {
 }
 
 hipError_t launch_attn_f32(const AttnF32Args& a, int d_k, hipStream_t s) {
+  if (a.group < 1 || a.h % a.group != 0) return hipErrorInvalidValue;
   if (d_k == 64) {
     dim3 grid((a.rows + 63) / 64, a.h, a.B);
     hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(ATTN32_NT), 0, s, a);

@@ -261,8 +261,9 @@ __device__ __forceinline__ int stage_chunk(int row, int c) {
   return RB == 128 ? (c ^ ((row >> 1) & 7)) : (c ^ (row & 15));
 }
 
-// Head-split epilogues of the QKV projection. Column n of [Q|K|V] is head
-// (n mod D) / d_k, channel (n mod D) mod d_k; row m is batch m / T, position
+// Head-split epilogues of the QKV projection. [Q|K|V] has a D-wide Q block
+// (h heads) and Dkv-wide K and V blocks (h_kv key/value sets); inside a block,
+// column c is head c / d_k, channel c mod d_k. Row m is batch m / T, position
 // m mod T. A wave's tile is staged in LDS and written back 16 bytes per lane,
 // so each store instruction covers whole contiguous lines; tiles that cross a
 // batch boundary or the matrix edge are stored directly from registers.
@@ -288,8 +289,10 @@ struct QkEpi {
     constexpr int WM = TM * 32, WN = TN * 32, RB = WN * 2, CPR = WN / 8;
     const int D = e.D, d_k = e.d_k, T = e.T, lq = lane & 31, lh = lane >> 5;
     const int bw = mbase / T, tw = mbase - bw * T;
-    // The wave's WN columns lie in one of Q or K (WN divides D).
-    const int ng0 = e.n_base + nbase, which = ng0 / D, hc0 = ng0 - which * D;
+    // The wave's WN columns lie in one of Q or K (WN divides D; the K block
+    // ends at N).
+    const int NQKV = D + 2 * e.Dkv;
+    const int ng0 = e.n_base + nbase, which = ng0 >= D ? 1 : 0, hc0 = ng0 - which * D;
     const float sc = which == 0 ? e.q_scale : 1.0f;
     // The wave's bias values, fetched together (one latency, not one per
     // fragment): lane columns ng0 + 32 j + 8 rg + 4 lh + 0..3 (clamped to the
@@ -323,7 +326,7 @@ struct QkEpi {
         const int m = mbase + i * 32 + lq;
         const int b = m / T, t = m - b * T;
         if (m < M && t < e.early_rows) {
-          float* er = e.early + ((size_t)b * e.early_rows + t) * (3 * D) + ng0;
+          float* er = e.early + ((size_t)b * e.early_rows + t) * NQKV + ng0;
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -360,6 +363,7 @@ struct QkEpi {
     // so consecutive lanes cover contiguous memory.
     const int hseg = min(WN, d_k), lg_cph = hseg == 128 ? 4 : 3;   // chunks per head segment
     const int tpad = which == 0 ? e.Tpad_q : e.Tpad_kv;
+    const int nheads = which == 0 ? e.h : e.h_kv;
     uint16_t* const dst = which == 0 ? e.q : e.k;
     const bool simple = tw + WM <= T && mbase + WM <= M && nbase + WN <= N;
 #pragma unroll 4
@@ -377,7 +381,7 @@ struct QkEpi {
         t = m - b * T;
       }
       __builtin_nontemporal_store(
-          val, reinterpret_cast<u32x4*>(dst + (((size_t)b * e.h + head) * tpad + t) * d_k + ch));
+          val, reinterpret_cast<u32x4*>(dst + (((size_t)b * nheads + head) * tpad + t) * d_k + ch));
     }
   }
 };
@@ -391,12 +395,13 @@ struct VEpi {
                                         int M, int N, uint8_t* lds) const {
     constexpr int WM = TM * 32, WN = TN * 32, RB = WM * 2, CPR = WM / 8;
     const int D = e.D, d_k = e.d_k, T = e.T, lq = lane & 31, lh = lane >> 5;
+    const int NQKV = D + 2 * e.Dkv, v0 = D + e.Dkv;   // V block starts at column v0
     const int bw = mbase / T, tw = mbase - bw * T;
     // One batch element, a full tile, and a start on a 16-position group so
     // the position permutation stays inside the tile.
     const bool staged = (tw & 15) == 0 && tw + WM <= T && mbase + WM <= M && nbase + WN <= N;
     if (staged) {
-      const int hc0 = e.n_base + nbase - 2 * D;
+      const int hc0 = e.n_base + nbase - v0;
       float bj[TN];   // the wave's bias values, fetched together
       if (e.bias) {
 #pragma unroll
@@ -422,7 +427,7 @@ struct VEpi {
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 if (tw + r0 + r < e.early_rows)
-                  e.early[((size_t)bw * e.early_rows + tw + r0 + r) * (3 * D) + ng] = v[r];
+                  e.early[((size_t)bw * e.early_rows + tw + r0 + r) * NQKV + ng] = v[r];
             }
             const int pos = vt_pos(r0);
             *reinterpret_cast<u32x2*>(lds + c * RB + stage_chunk<RB>(c, pos >> 3) * 16 +
@@ -439,7 +444,7 @@ struct VEpi {
         const u32x4 val = *reinterpret_cast<const u32x4*>(lds + c * RB + stage_chunk<RB>(c, p8) * 16);
         const int col = hc0 + c, head = col / d_k, ch = col - head * d_k;
         __builtin_nontemporal_store(
-            val, reinterpret_cast<u32x4*>(e.vt + (((size_t)bw * e.h + head) * d_k + ch) * e.Tpad_kv +
+            val, reinterpret_cast<u32x4*>(e.vt + (((size_t)bw * e.h_kv + head) * d_k + ch) * e.Tpad_kv +
                                           tw + p8 * 8));
       }
       return;
@@ -449,7 +454,7 @@ struct VEpi {
       const int n = nbase + j * 32 + lq;
       if (n >= N) continue;
       const int ng = e.n_base + n;
-      const int hc = ng - 2 * D, head = hc / d_k, c = hc - head * d_k;
+      const int hc = ng - v0, head = hc / d_k, c = hc - head * d_k;
       const float bias = load_bias_bf16(e.bias, ng);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -466,8 +471,8 @@ struct VEpi {
             if (m >= M) break;
             const int b = m / T, t = m - b * T;
             if (e.early && t < e.early_rows)
-              e.early[((size_t)b * e.early_rows + t) * (3 * D) + ng] = v[r];
-            e.vt[(((size_t)b * e.h + head) * d_k + c) * e.Tpad_kv + vt_pos(t)] =
+              e.early[((size_t)b * e.early_rows + t) * NQKV + ng] = v[r];
+            e.vt[(((size_t)b * e.h_kv + head) * d_k + c) * e.Tpad_kv + vt_pos(t)] =
                 float_to_f16_bits(v[r]);
           }
         }
@@ -651,7 +656,7 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
                            const QkvEpilogue& e, hipStream_t s) {
   // Columns [n_base, n_base + N) of [Q|K|V]: the Q and K part runs with
   // transposed tiles, the V part with normal tiles.
-  const int n_lo = e.n_base, n_hi = e.n_base + N, split = 2 * e.D;
+  const int n_lo = e.n_base, n_hi = e.n_base + N, split = e.D + e.Dkv;
   if (n_lo < split) {
     QkEpi epi{e};
     const hipError_t err = launch_qkv_part<true>(A, M, K, Bt, min(n_hi, split) - n_lo, epi, s);

@@ -20,18 +20,21 @@ hipError_t launch_transpose_bf16(const uint16_t* W, int K, int N, uint16_t* WT, 
 hipError_t launch_mask_extent(const uint8_t* mask, int B, int T_k, int* kend, hipStream_t s);
 
 // ---- 16-bit MFMA GEMMs (C = A . Bt^T, both operands K-contiguous) -------
+// Columns of [Q | K | V]: Q is D wide (h heads), K and V are Dkv = h_kv * d_k
+// wide each (h_kv key/value sets); N_qkv = D + 2 Dkv.
 struct QkvEpilogue {
   int T;                 // rows of A per batch element (m = b*T + t)
   int Tpad_q;            // padded sequence length of the q buffer
   int Tpad_kv;           // padded sequence length of the k and vt buffers
   int D, h, d_k;
-  int n_base;            // global column (0..3D) of GEMM column 0
-  const uint16_t* bias;  // (3D) bf16, or null
+  int h_kv, Dkv;         // key/value sets and the width of the K and V blocks
+  int n_base;            // global column (0..N_qkv) of GEMM column 0
+  const uint16_t* bias;  // (N_qkv) bf16, or null
   uint16_t* q;           // (B, h, Tpad_q, d_k) fp16 -- columns [0, D)
-  uint16_t* k;           // (B, h, Tpad_kv, d_k) fp16 -- columns [D, 2D)
-  uint16_t* vt;          // (B, h, d_k, Tpad_kv) fp16 -- columns [2D, 3D), transposed;
-                         // position t stored at vt_pos(t) (bits 2 and 3 swapped)
-  float* early;          // (B, early_rows, 3D) fp32 copy of rows t < early_rows, or null
+  uint16_t* k;           // (B, h_kv, Tpad_kv, d_k) fp16 -- columns [D, D + Dkv)
+  uint16_t* vt;          // (B, h_kv, d_k, Tpad_kv) fp16 -- columns [D + Dkv, N_qkv),
+                         // transposed; position t stored at vt_pos(t) (bits 2 and 3 swapped)
+  float* early;          // (B, early_rows, N_qkv) fp32 copy of rows t < early_rows, or null
   int early_rows;
   float q_scale;         // multiplies the fp16 Q (the fp32 early copy is unscaled)
 };
@@ -50,13 +53,13 @@ hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT,
 // ---- fused attention, fp16 operands, fp32 softmax state ------------------
 struct AttnF16Args {
   const uint16_t* q;   // (B, h, Tqp, d_k) fp16, pre-multiplied by log2(e)/sqrt(d_k)
-  const uint16_t* k;   // (B, h, Tkp, d_k) fp16
-  const uint16_t* vt;  // (B, h, d_k, Tkp) fp16, positions permuted as the QKV epilogue stores them
+  const uint16_t* k;   // (B, h_kv, Tkp, d_k) fp16; query head i reads set i / (h / h_kv)
+  const uint16_t* vt;  // (B, h_kv, d_k, Tkp) fp16, positions permuted as the QKV epilogue stores them
   uint16_t* o;         // (B, T_q, D) fp16, head i at columns [i*d_k, (i+1)*d_k)
   const uint32_t* mbits;  // (B, mbits_ld, 2) ignore bitmask per 64-key tile, or null
   int mbits_ld;           // 64-key tiles per batch element (attn_mask_tiles(T_k))
   const int* kend;     // (B) key extent from the mask; read only with mbits
-  int B, h, T_q, T_k, Tqp, Tkp, D, causal;
+  int B, h, h_kv, T_q, T_k, Tqp, Tkp, D, causal;
 };
 int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp, Tkp must be multiples)
 int attn_mask_tiles(int T_k);    // 64-key tiles covering T_k
@@ -74,7 +77,9 @@ hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B,
 
 struct AttnF32Args {
   const float* q; long q_bstride; int q_ld;    // q[b*q_bstride + t*q_ld + head*d_k + c]
+  // k[b*kv_bstride + t*kv_ld + (head/group)*d_k + c], likewise v
   const float* k; const float* v; long kv_bstride; int kv_ld;
+  int group;                                    // query heads per key/value set (>= 1)
   float* o; long o_bstride; int o_ld;
   const uint8_t* mask;                          // (B, mask_ld) nonzero = ignore, or null
   int mask_ld;

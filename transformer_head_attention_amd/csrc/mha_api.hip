@@ -10,7 +10,8 @@
 //              the padding mask.
 //   qkv_proj   [Q|K|V] = X . W_QKV + b (cross-attention: Q from x_q,
 //              K and V from x_kv), fp32 accumulate, head split into fp16
-//              Q, K (B,h,T,d_k) and V^T (B,h,d_k,T).
+//              Q (B,h,T,d_k), K (B,h_kv,T,d_k) and V^T (B,h_kv,d_k,T), h_kv
+//              being the number of key/value sets (h unless grouped).
 //   attention  fused masked softmax(QK^T/sqrt(d_k)) V -> O (B,T_q,D) fp16.
 //   out_proj   Y = O . W_O + b_O, fp32.
 //   early_rows causal only: rows t < 64 of every sequence, which average
@@ -33,6 +34,9 @@
 
 struct mha_handle {
   int D, h, d_k;
+  int h_kv;      // key/value sets (h for plain multi-head attention)
+  int Dkv;       // h_kv * d_k: width of the K and of the V block of [Q|K|V]
+  int Nqkv;      // D + 2 Dkv
   mha_dtype_t dtype;
   // profiling state
   int prof_max = 0;
@@ -70,20 +74,22 @@ Layout make_layout(const mha_handle* hd, int B, int T_q, int T_k) {
     L.Tqp = round_up(T_q, bm);
     L.Tkp = round_up(T_k, bm);
     L.R = std::min(mha::kEarlyRows, T_q);
-    L.wqkvT = take(3 * D * D * 2);
+    const size_t Dkv = (size_t)hd->Dkv, Nqkv = (size_t)hd->Nqkv;
+    L.wqkvT = take(Nqkv * D * 2);
     L.woT = take(D * D * 2);
     L.q = take((size_t)B * L.Tqp * D * 2);
-    L.k = take((size_t)B * L.Tkp * D * 2);
-    L.vt = take((size_t)B * L.Tkp * D * 2);
+    L.k = take((size_t)B * L.Tkp * Dkv * 2);
+    L.vt = take((size_t)B * L.Tkp * Dkv * 2);
     L.o = take((size_t)B * T_q * D * 2);
     L.kend = take((size_t)B * 4);
     L.mbits = take((size_t)B * mha::attn_mask_tiles(T_k) * 8);
-    L.eqkv = take((size_t)B * L.R * 3 * D * 4);
+    L.eqkv = take((size_t)B * L.R * Nqkv * 4);
     L.eo = take((size_t)B * L.R * D * 4);
   } else {
-    // One region: self-attention uses it as a single (B*T, 3D) buffer;
-    // cross-attention as Q (B*T_q, D) followed by [K|V] (B*T_k, 2D).
-    L.f_q = take((size_t)B * T_q * D * 4 + (size_t)B * T_k * 2 * D * 4);
+    // One region: self-attention uses it as a single (B*T, N_qkv) buffer;
+    // cross-attention as Q (B*T_q, D) followed by [K|V] (B*T_k, 2 Dkv).
+    const size_t Dkv = (size_t)hd->Dkv;
+    L.f_q = take((size_t)B * T_q * D * 4 + (size_t)B * T_k * 2 * Dkv * 4);
     L.f_kv = L.f_q + (size_t)B * T_q * D * 4;
     L.f_o = take((size_t)B * T_q * D * 4);
   }
@@ -121,9 +127,15 @@ thread_local hipError_t g_last_hip_error = hipSuccess;
 extern "C" {
 
 mha_status_t mha_create(mha_handle_t* out, int d_model, int num_heads, mha_dtype_t dtype) {
+  return mha_create_grouped(out, d_model, num_heads, num_heads, dtype);
+}
+
+mha_status_t mha_create_grouped(mha_handle_t* out, int d_model, int num_heads, int num_kv_heads,
+                                mha_dtype_t dtype) {
   if (!out) return MHA_ERR_INVALID_ARG;
   *out = nullptr;
   if (d_model <= 0 || num_heads <= 0 || d_model % num_heads != 0) return MHA_ERR_INVALID_ARG;
+  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0) return MHA_ERR_INVALID_ARG;
   if (dtype != MHA_F32 && dtype != MHA_BF16) return MHA_ERR_INVALID_ARG;
   const int d_k = d_model / num_heads;
   if ((d_k != 64 && d_k != 128) || d_model % 128 != 0) return MHA_ERR_UNSUPPORTED;
@@ -132,6 +144,9 @@ mha_status_t mha_create(mha_handle_t* out, int d_model, int num_heads, mha_dtype
   hd->D = d_model;
   hd->h = num_heads;
   hd->d_k = d_k;
+  hd->h_kv = num_kv_heads;
+  hd->Dkv = num_kv_heads * d_k;
+  hd->Nqkv = d_model + 2 * hd->Dkv;
   hd->dtype = dtype;
   *out = hd;
   return MHA_OK;
@@ -226,7 +241,8 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
 
   hipStream_t s = static_cast<hipStream_t>(stream_);
   char* ws = static_cast<char*>(workspace);
-  const int D = hd->D, h = hd->h, d_k = hd->d_k;
+  const int D = hd->D, h = hd->h, d_k = hd->d_k, h_kv = hd->h_kv, Dkv = hd->Dkv,
+            Nqkv = hd->Nqkv;
   const bool cross = x_kv != nullptr;
 
   // stage boundary events (measurement only)
@@ -262,7 +278,7 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     const uint16_t* bq = static_cast<const uint16_t*>(b_qkv);
 
     // prep
-    MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_qkv), D, 3 * D, wqkvT,
+    MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_qkv), D, Nqkv, wqkvT,
                                        false, s));
     MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_o), D, D, woT, true, s));
     if (key_padding_mask) {
@@ -278,6 +294,8 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     e.D = D;
     e.h = h;
     e.d_k = d_k;
+    e.h_kv = h_kv;
+    e.Dkv = Dkv;
     e.bias = bq;
     e.q = q;
     e.k = k;
@@ -290,14 +308,14 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     if (!cross) {
       e.T = T_q;
       e.n_base = 0;
-      MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wqkvT, 3 * D, e, s));
+      MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wqkvT, Nqkv, e, s));
     } else {
       e.T = T_q;
       e.n_base = 0;
       MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wqkvT, D, e, s));
       e.T = T_k;
       e.n_base = D;
-      MHA_HIP(mha::launch_gemm_qkv(xkv, B * T_k, D, wqkvT + (size_t)D * D, 2 * D, e, s));
+      MHA_HIP(mha::launch_gemm_qkv(xkv, B * T_k, D, wqkvT + (size_t)D * D, 2 * Dkv, e, s));
     }
     if (!mark(2)) return MHA_ERR_HIP;
 
@@ -312,6 +330,7 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     a.kend = key_padding_mask ? kend : nullptr;
     a.B = B;
     a.h = h;
+    a.h_kv = h_kv;
     a.T_q = T_q;
     a.T_k = T_k;
     a.Tqp = L.Tqp;
@@ -330,9 +349,10 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
       mha::AttnF32Args f{};
       f.q = eqkv;
       f.k = eqkv + D;
-      f.v = eqkv + 2 * D;
-      f.q_ld = f.kv_ld = 3 * D;
-      f.q_bstride = f.kv_bstride = (long)L.R * 3 * D;
+      f.v = eqkv + D + Dkv;
+      f.q_ld = f.kv_ld = Nqkv;
+      f.q_bstride = f.kv_bstride = (long)L.R * Nqkv;
+      f.group = h / h_kv;
       f.o = eo;
       f.o_ld = D;
       f.o_bstride = (long)L.R * D;
@@ -360,27 +380,28 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
 
     mha::AttnF32Args f{};
     if (!cross) {
-      // one (B*T, 3D) product; Q, K, V are column blocks of it
-      MHA_HIP(mha::launch_gemm_f32(xq, D, B * T_q, D, W, 3 * D, 3 * D, false, bqkv, fq, 3 * D,
+      // one (B*T, N_qkv) product; Q, K, V are column blocks of it
+      MHA_HIP(mha::launch_gemm_f32(xq, D, B * T_q, D, W, Nqkv, Nqkv, false, bqkv, fq, Nqkv,
                                    B * T_q, B * T_q, s));
       f.q = fq;
       f.k = fq + D;
-      f.v = fq + 2 * D;
-      f.q_ld = f.kv_ld = 3 * D;
-      f.q_bstride = f.kv_bstride = (long)T_q * 3 * D;
+      f.v = fq + D + Dkv;
+      f.q_ld = f.kv_ld = Nqkv;
+      f.q_bstride = f.kv_bstride = (long)T_q * Nqkv;
     } else {
-      MHA_HIP(mha::launch_gemm_f32(xq, D, B * T_q, D, W, 3 * D, D, false, bqkv, fq, D, B * T_q,
+      MHA_HIP(mha::launch_gemm_f32(xq, D, B * T_q, D, W, Nqkv, D, false, bqkv, fq, D, B * T_q,
                                    B * T_q, s));
-      MHA_HIP(mha::launch_gemm_f32(xkv, D, B * T_k, D, W + D, 3 * D, 2 * D, false,
-                                   bqkv ? bqkv + D : nullptr, fkv, 2 * D, B * T_k, B * T_k, s));
+      MHA_HIP(mha::launch_gemm_f32(xkv, D, B * T_k, D, W + D, Nqkv, 2 * Dkv, false,
+                                   bqkv ? bqkv + D : nullptr, fkv, 2 * Dkv, B * T_k, B * T_k, s));
       f.q = fq;
       f.q_ld = D;
       f.q_bstride = (long)T_q * D;
       f.k = fkv;
-      f.v = fkv + D;
-      f.kv_ld = 2 * D;
-      f.kv_bstride = (long)T_k * 2 * D;
+      f.v = fkv + Dkv;
+      f.kv_ld = 2 * Dkv;
+      f.kv_bstride = (long)T_k * 2 * Dkv;
     }
+    f.group = h / h_kv;
     if (!mark(2)) return MHA_ERR_HIP;
     f.o = fo;
     f.o_ld = D;
