@@ -78,3 +78,38 @@ def brute_force_mha(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
             y_b.append(_matvec(o_cat, w_o, 0, D, b_o))
         y_all.append(y_b)
     return y_all
+
+
+def brute_force_decode(x_new, w_qkv, b_qkv, w_o, b_o, h, k_cache, v_cache, cache_len,
+                       n_kv_heads=None):
+    """One generation step from nested lists: y[b][j][c] for new token j of
+    batch b at position cache_len[b] + j. Its keys are the cached rows
+    k_cache[b][g][0 .. cache_len[b]-1] followed by the new tokens 0..j, each
+    new key and value projected from x_new (iamjaehka13.blog §21: the cache
+    holds earlier tokens' keys and values)."""
+    D = len(w_qkv)
+    d = D // h
+    n_g = h if n_kv_heads is None else n_kv_heads
+    per_group = h // n_g
+    y_all = []
+    for b in range(len(x_new)):
+        L = cache_len[b]
+        y_b = []
+        for j in range(len(x_new[b])):
+            o_cat = []
+            for head in range(h):
+                g = head // per_group
+                q = _matvec(x_new[b][j], w_qkv, head * d, d, b_qkv)
+                keys = [k_cache[b][g][p] for p in range(L)]
+                vals = [v_cache[b][g][p] for p in range(L)]
+                for jj in range(j + 1):
+                    keys.append(_matvec(x_new[b][jj], w_qkv, D + g * d, d, b_qkv))
+                    vals.append(_matvec(x_new[b][jj], w_qkv, D + n_g * d + g * d, d, b_qkv))
+                weights = [math.exp(sum(q[c] * kk[c] for c in range(d)) / math.sqrt(d))
+                           for kk in keys]
+                total = sum(weights)
+                o = [sum(wt * vv[c] for wt, vv in zip(weights, vals)) / total for c in range(d)]
+                o_cat.extend(o)
+            y_b.append(_matvec(o_cat, w_o, 0, D, b_o))
+        y_all.append(y_b)
+    return y_all

@@ -26,6 +26,10 @@ Sources (pages as titled; sections / equations named, no line numbers):
   key/value sets, each shared by a group of query heads; the key/value
   elements per token and layer are 2 n_h d_h (MHA), 2 d_h (MQA), 2 n_g d_h
   (GQA).
+* Same itwiki section, first paragraph, and iamjaehka13.blog §21: during
+  autoregressive generation the keys and values of earlier tokens are kept in
+  a KV cache, so a step computes only the new tokens' projections and reads
+  every cached key and value.
 
 Conventions (readings where the pages leave a step open):
 
@@ -210,6 +214,42 @@ def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
         o, _ = _attend_grouped(qh, kh, vh, n_g, causal, mask_b, q_pos=ts)
         out[b] = linear(concat_heads(o), w_o, b_o)[0]
     return out
+
+
+def mha_decode(x_new, w_qkv, b_qkv, w_o, b_o, h, k_cache, v_cache, cache_len,
+               n_kv_heads=None):
+    """One generation step against a KV cache, batch-first.
+
+    x_new (B, T_new, D): the new tokens; batch element b holds positions
+    cache_len[b] .. cache_len[b] + T_new - 1. k_cache, v_cache (B, n_g, T_max,
+    d_k): rows [0, cache_len[b]) of batch b are the keys and values of its
+    earlier tokens (later rows are ignored). The new tokens' keys and values
+    are projected from x_new and appended after the cached ones; new token j
+    attends to every cached key and to new tokens 0..j (the causal mask at its
+    position). Returns (y (B, T_new, D), k_new, v_new (B, n_g, T_new, d_k)),
+    k_new and v_new being what the step appends to the cache.
+    """
+    x_new, w_qkv, b_qkv, w_o, b_o = map(_as64, (x_new, w_qkv, b_qkv, w_o, b_o))
+    k_cache, v_cache = _as64(k_cache), _as64(v_cache)
+    B, T_new, D = x_new.shape
+    if D % h != 0:
+        raise ValueError("embed_dim must be divisible by num_heads")
+    n_g = _kv_width(w_qkv, D, h, n_kv_heads)
+    q, k, v = _qkv(x_new, None, w_qkv, b_qkv, D)
+    qh = split_heads(q, h)
+    k_new, v_new = split_heads(k, n_g), split_heads(v, n_g)
+    lens = np.asarray(cache_len, dtype=np.int64)
+    o = np.empty_like(qh)
+    for b in range(B):
+        L = int(lens[b])
+        if L < 0 or L > k_cache.shape[2]:
+            raise ValueError("cache_len out of range")
+        kb = np.concatenate([k_cache[b, :, :L], k_new[b]], axis=1)[None]
+        vb = np.concatenate([v_cache[b, :, :L], v_new[b]], axis=1)[None]
+        o[b:b + 1], _ = _attend_grouped(qh[b:b + 1], kb, vb, n_g, True, None,
+                                        q_pos=L + np.arange(T_new))
+    y = linear(concat_heads(o), w_o, b_o)
+    return y, k_new, v_new
 
 
 def param_count(D: int, h: int, bias: bool = True, n_kv_heads=None) -> int:
