@@ -125,6 +125,45 @@ mha_status_t mha_forward(mha_handle_t handle,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* ---- Generation step against a KV cache ----------------------------------
+ * itwiki "멀티 헤드 어텐션", section 추론 비용과 변형 (autoregressive
+ * generation keeps earlier tokens' keys and values in a KV cache and reads
+ * all of it at every step), iamjaehka13.blog "[Deep Learning 5]", §21.
+ *
+ * Batch element b holds cache_len[b] earlier tokens; the step takes T_new
+ * new tokens at positions cache_len[b] .. cache_len[b] + T_new - 1:
+ *   [Q | K | V] = x W_QKV + b_QKV for the new tokens only; new token j
+ *   attends to the cached keys 0 .. cache_len[b]-1 and to new tokens 0 .. j
+ *   (causal); y = Concat(heads) W_O + b_O.
+ * The new tokens' keys and values are written into the caches at rows
+ * cache_len[b] .. cache_len[b] + T_new - 1, rounded to bf16 (round to
+ * nearest even); the step's own attention uses them unrounded (fp32).
+ *
+ *   x          (B, T_new, D)          bf16   the new tokens
+ *   w_qkv, b_qkv, w_o, b_o                   as mha_forward (b_* may be NULL)
+ *   k_cache    (B, n_g, T_max, d_k)   bf16   DEVICE, read rows [0, len),
+ *   v_cache    (B, n_g, T_max, d_k)   bf16   written rows [len, len + T_new)
+ *   cache_len  (B)                    int32  DEVICE; must satisfy
+ *              0 <= cache_len[b] <= T_max - T_new. Not modified (advance it
+ *              by T_new after the step). Values outside are clamped into
+ *              that range by the kernels (no out-of-bounds access; the
+ *              result is then that of the clamped length).
+ *   y          (B, T_new, D)          fp32   output, fully overwritten
+ *   workspace  >= mha_decode_workspace_size(handle, B, T_new, T_max) bytes
+ * Requires a MHA_BF16 handle (MHA_ERR_UNSUPPORTED otherwise), 1 <= T_new <=
+ * T_max, B <= 65535; data pointers 16-byte aligned, cache_len 4-byte
+ * aligned. Stream, ownership and error behaviour as mha_forward; stage
+ * timing records "qkv_proj", "attention" and "out_proj". */
+size_t mha_decode_workspace_size(mha_handle_t handle, int B, int T_new, int T_max);
+mha_status_t mha_decode(mha_handle_t handle, const void* x,
+                        const void* w_qkv, const void* b_qkv,
+                        const void* w_o, const void* b_o,
+                        int B, int T_new,
+                        void* k_cache, void* v_cache, int T_max, const int* cache_len,
+                        float* y,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* Release a handle (NULL is accepted). */
 mha_status_t mha_destroy(mha_handle_t handle);
 

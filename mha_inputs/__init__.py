@@ -189,6 +189,106 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     return out
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One generation step against a KV cache (bf16): B sequences with
+    cached lengths drawn uniformly from ``lengths`` (inclusive), T_new new
+    tokens each, caches of capacity T_max."""
+
+    name: str
+    D: int
+    h: int
+    B: int
+    T_new: int
+    T_max: int
+    lengths: tuple
+    n_kv: Optional[int] = None
+    bias_std: Optional[float] = 0.02
+    dtype: str = "bf16"
+
+    @property
+    def d_k(self) -> int:
+        return self.D // self.h
+
+    @property
+    def n_g(self) -> int:
+        return self.h if self.n_kv is None else self.n_kv
+
+    @property
+    def n_qkv(self) -> int:
+        return self.D + 2 * self.n_g * self.d_k
+
+    def flops(self, lengths) -> float:
+        """Projections of the new tokens (2 D N_qkv + 2 D^2 per token) plus
+        scores and weighted sum over (cached + causal new) keys, 4 d_k per
+        (query head, key) pair."""
+        tok = self.B * self.T_new
+        proj = tok * (2.0 * self.D * self.n_qkv + 2.0 * self.D * self.D)
+        pairs = sum(int(L) * self.T_new + self.T_new * (self.T_new + 1) // 2 for L in lengths)
+        return proj + 4.0 * self.d_k * self.h * pairs
+
+    def cache_bytes(self, lengths) -> float:
+        """bf16 key and value bytes a step must read (cached rows only)."""
+        return 2.0 * 2.0 * self.n_g * self.d_k * float(sum(int(L) for L in lengths))
+
+    def shrink(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        DecodeWorkload("decode_bf16_d1024_h16_b32_t4096", 1024, 16, 32, 1, 4096, (2048, 4095)),
+        DecodeWorkload("decode_gqa4_bf16_d1024_h16_b32_t4096", 1024, 16, 32, 1, 4096,
+                       (2048, 4095), n_kv=4),
+        DecodeWorkload("decode_mqa_bf16_d1024_h16_b32_t4096", 1024, 16, 32, 1, 4096,
+                       (2048, 4095), n_kv=1),
+        DecodeWorkload("decode_bf16_d4096_h32_b8_t8192", 4096, 32, 8, 1, 8192, (4096, 8191),
+                       bias_std=None),
+    ]
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: int = 0) -> dict:
+    """Draw a generation step's inputs on the CPU (bf16 tensors, int32 lengths).
+
+    Draw order: x_new, W_QKV, W_O, b_QKV, b_O, lengths, K cache, V cache.
+    Weights are Xavier-uniform as for the forward workloads; cached keys and
+    values are N(0, s) with s the standard deviation of a projected value
+    under those distributions, sqrt(D a^2 / 3) for the W_QKV bound a. Cache
+    rows at or past a sequence's length are filled with NaN: they must never
+    be read.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    D, n_qkv = w.D, w.n_qkv
+    x = _normal(g, (w.B, w.T_new, D), 1.0)
+    a = math.sqrt(6.0 / (D + n_qkv))
+    w_qkv = _uniform(g, (D, n_qkv), a)
+    w_o = _uniform(g, (D, D), math.sqrt(6.0 / (D + D)))
+    if w.bias_std is None:
+        b_qkv, b_o = torch.zeros(n_qkv), torch.zeros(D)
+    else:
+        b_qkv = _normal(g, (n_qkv,), w.bias_std)
+        b_o = _normal(g, (D,), w.bias_std)
+    lo, hi = w.lengths
+    if not 0 <= lo <= hi <= w.T_max - w.T_new:
+        raise ValueError("cached lengths must lie in [0, T_max - T_new]")
+    lengths = torch.randint(lo, hi + 1, (w.B,), generator=g).to(torch.int32)
+    s = math.sqrt(D * a * a / 3.0)
+    shape = (w.B, w.n_g, w.T_max, w.d_k)
+    k_cache = _normal(g, shape, s)
+    v_cache = _normal(g, shape, s)
+    pos = torch.arange(w.T_max)
+    unused = (pos[None, :] >= lengths[:, None].long())[:, None, :, None]
+    k_cache = torch.where(unused, torch.full_like(k_cache, float("nan")), k_cache)
+    v_cache = torch.where(unused, torch.full_like(v_cache, float("nan")), v_cache)
+    dt = torch.bfloat16
+    return {"x": x.to(dt), "w_qkv": w_qkv.to(dt), "w_o": w_o.to(dt), "b_qkv": b_qkv.to(dt),
+            "b_o": b_o.to(dt), "k_cache": k_cache.to(dt), "v_cache": v_cache.to(dt),
+            "cache_len": lengths, "h": w.h, "n_kv": w.n_g}
+
+
 def as_float64_numpy(t):
     """Exact upcast of a (bf16 or fp32) CPU tensor to a float64 numpy array."""
     if t is None:

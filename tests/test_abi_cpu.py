@@ -151,3 +151,36 @@ def test_create_grouped_validation_and_workspace(mha):
         assert st == mha.MHA_OK
         assert mha.mha_workspace_size(h, 2, 100, 300) > 0
         mha.mha_destroy(h)
+
+
+def test_decode_validation_without_device_work(mha):
+    st, h = mha.mha_create_grouped(1024, 16, 4, mha.MHA_BF16)
+    st2, h32 = mha.mha_create(512, 8, mha.MHA_F32)
+    fake = 1 << 20
+    try:
+        ws = mha.mha_decode_workspace_size(h, 4, 2, 128)
+        assert ws > 0 and ws % 256 == 0
+        assert mha.mha_decode_workspace_size(h, 4, 3, 2) == 0        # T_new > T_max
+        assert mha.mha_decode_workspace_size(h, 0, 1, 128) == 0
+        assert mha.mha_decode_workspace_size(h32, 4, 1, 128) == 0    # bf16 handles only
+
+        def call(handle=h, **kw):
+            args = dict(x=fake, w_qkv=fake, b_qkv=None, w_o=fake, b_o=None, B=4, T_new=2,
+                        k_cache=fake, v_cache=fake, T_max=128, cache_len=fake, y=fake,
+                        workspace=fake, workspace_bytes=ws, stream=None)
+            args.update(kw)
+            return mha.mha_decode(handle, *args.values())
+
+        assert call(handle=None) == mha.MHA_ERR_INVALID_ARG
+        assert call(k_cache=None) == mha.MHA_ERR_INVALID_ARG
+        assert call(cache_len=None) == mha.MHA_ERR_INVALID_ARG
+        assert call(cache_len=fake + 2) == mha.MHA_ERR_INVALID_ARG   # misaligned lengths
+        assert call(v_cache=fake + 8) == mha.MHA_ERR_INVALID_ARG     # misaligned cache
+        assert call(T_new=0) == mha.MHA_ERR_INVALID_ARG
+        assert call(T_new=129) == mha.MHA_ERR_INVALID_ARG
+        assert call(B=70000) == mha.MHA_ERR_INVALID_ARG
+        assert call(workspace_bytes=ws - 1) == mha.MHA_ERR_WORKSPACE
+        assert call(handle=h32) == mha.MHA_ERR_UNSUPPORTED
+    finally:
+        mha.mha_destroy(h)
+        mha.mha_destroy(h32)

@@ -85,3 +85,21 @@ def test_grouped_workloads_shapes_and_flops():
     # plain MHA draws are unchanged by the grouped-head field
     small = WORKLOADS[HEADLINE].shrink(B=1, T_q=8, T_k=8)
     assert make_inputs(small, 0)["w_qkv"].shape == (1024, 3072)
+
+
+def test_decode_inputs_shapes_lengths_and_unused_rows():
+    from mha_inputs import DECODE_WORKLOADS, make_decode_inputs
+    import pytest
+    for name, w in DECODE_WORKLOADS.items():
+        small = w.shrink(B=3, T_max=96, lengths=(0, 96 - w.T_new))
+        inp = make_decode_inputs(small, 0)
+        assert inp["x"].shape == (3, w.T_new, w.D) and inp["x"].dtype == torch.bfloat16
+        assert inp["w_qkv"].shape == (w.D, w.n_qkv)
+        assert inp["k_cache"].shape == (3, w.n_g, 96, w.d_k)
+        L = inp["cache_len"]
+        assert L.dtype == torch.int32 and ((L >= 0) & (L <= 96 - w.T_new)).all()
+        for b in range(3):
+            assert torch.isnan(inp["k_cache"][b, :, int(L[b]):].float()).all()
+            assert torch.isfinite(inp["v_cache"][b, :, :int(L[b])].float()).all()
+    with pytest.raises(ValueError):
+        make_decode_inputs(w.shrink(T_max=64, lengths=(0, 64)), 0)

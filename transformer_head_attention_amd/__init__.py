@@ -34,6 +34,7 @@ MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP
 MHA_NUM_STAGES = 5
 
 EXPORTED = ("mha_create", "mha_create_grouped", "mha_workspace_size", "mha_forward", "mha_destroy",
+            "mha_decode_workspace_size", "mha_decode",
             "mha_status_string", "mha_hip_error_string", "mha_profile_begin", "mha_profile_end",
             "mha_stage_name")
 
@@ -47,6 +48,11 @@ _lib.mha_workspace_size.restype = _sz
 _lib.mha_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
                              _vp, _vp, _sz, _vp]
 _lib.mha_forward.restype = _int
+_lib.mha_decode_workspace_size.argtypes = [_vp, _int, _int, _int]
+_lib.mha_decode_workspace_size.restype = _sz
+_lib.mha_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _vp, _vp, _int, _vp, _vp,
+                            _vp, _sz, _vp]
+_lib.mha_decode.restype = _int
 _lib.mha_destroy.argtypes = [_vp]
 _lib.mha_destroy.restype = _int
 _lib.mha_status_string.argtypes = [_int]
@@ -115,6 +121,18 @@ def mha_forward(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k, causal,
     return _lib.mha_forward(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, int(B), int(T_q),
                             int(T_k), int(causal), key_padding_mask, y, workspace,
                             int(workspace_bytes), stream)
+
+
+def mha_decode_workspace_size(handle, B: int, T_new: int, T_max: int) -> int:
+    return int(_lib.mha_decode_workspace_size(handle, int(B), int(T_new), int(T_max)))
+
+
+def mha_decode(handle, x, w_qkv, b_qkv, w_o, b_o, B, T_new, k_cache, v_cache, T_max, cache_len,
+               y, workspace, workspace_bytes, stream) -> int:
+    """Raw call: every pointer argument is an int device address (or 0/None)."""
+    return _lib.mha_decode(handle, x, w_qkv, b_qkv, w_o, b_o, int(B), int(T_new), k_cache,
+                           v_cache, int(T_max), cache_len, y, workspace, int(workspace_bytes),
+                           stream)
 
 
 def mha_destroy(handle) -> int:
@@ -227,3 +245,44 @@ class MultiHeadAttention:
         return out
 
     __call__ = forward
+
+    def decode(self, x, w_qkv, w_o, k_cache, v_cache, cache_len, b_qkv=None, b_o=None, out=None,
+               workspace=None, stream=None):
+        """One generation step: x (B, T_new, D) bf16; k_cache, v_cache
+        (B, num_kv_heads, T_max, d_k) bf16, rows [len, len + T_new) written;
+        cache_len (B,) int32 on the device, not modified. Returns y (B, T_new, D)
+        fp32."""
+        torch = self._torch
+        if x.dim() != 3:
+            raise ValueError("x must be (B, T_new, D)")
+        B, T_new, D = x.shape
+        d_k = D // self.num_heads
+        if k_cache.dim() != 4:
+            raise ValueError("caches must be (B, num_kv_heads, T_max, d_k)")
+        T_max = k_cache.shape[2]
+        self._check_shapes(x, w_qkv, w_o, b_qkv, b_o, None, None, out)
+        for c in (k_cache, v_cache):
+            if tuple(c.shape) != (B, self.num_kv_heads, T_max, d_k):
+                raise ValueError(f"cache shape {tuple(c.shape)} != "
+                                 f"{(B, self.num_kv_heads, T_max, d_k)}")
+        if tuple(cache_len.shape) != (B,) or cache_len.dtype != torch.int32:
+            raise ValueError("cache_len must be an int32 tensor of shape (B,)")
+        if out is None:
+            out = torch.empty(B, T_new, D, dtype=torch.float32, device=x.device)
+        n = mha_decode_workspace_size(self.handle, B, T_new, T_max)
+        if n == 0:
+            raise MHAError(MHA_ERR_INVALID_ARG, "mha_decode_workspace_size")
+        if workspace is None:
+            if self._ws is None or self._ws.numel() < n or self._ws.device != x.device:
+                self._ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+            workspace = self._ws
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        dt = self._tdtype
+        st = mha_decode(self.handle, self._ptr(x, dt), self._ptr(w_qkv, dt), self._ptr(b_qkv, dt),
+                        self._ptr(w_o, dt), self._ptr(b_o, dt), B, T_new, self._ptr(k_cache, dt),
+                        self._ptr(v_cache, dt), T_max, self._ptr(cache_len, torch.int32),
+                        self._ptr(out, torch.float32), workspace.data_ptr(), workspace.numel(),
+                        stream)
+        _check(st, "mha_decode")
+        return out

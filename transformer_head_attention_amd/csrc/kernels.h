@@ -89,4 +89,36 @@ hipError_t launch_attn_f32(const AttnF32Args& a, int d_k, hipStream_t s);
 // rows <= T_k <= 64 (the first rows of causal sequences).
 hipError_t launch_attn_early(const AttnF32Args& a, int d_k, hipStream_t s);
 
+// ---- generation step against a KV cache (bf16 handles) ------------------
+struct DecodeArgs {
+  int B, T_new, T_max, D, h, h_kv, d_k, Dkv;
+  float q_scale;              // log2(e) / sqrt(d_k)
+  const uint16_t* b_qkv;      // (D + 2 Dkv) bf16 or null
+  const int* cache_len;       // (B) valid cached rows, clamped to [0, T_max - T_new]
+  uint16_t* k_cache;          // (B, h_kv, T_max, d_k) bf16; rows [len, len + T_new) written
+  uint16_t* v_cache;          // (B, h_kv, T_max, d_k) bf16
+  float* q32;                 // (B*T_new, D) pre-scaled Q
+  uint16_t* q16;              // (B, h, T_new, d_k) fp16 pre-scaled Q
+  float* k32;                 // (B*T_new, Dkv) this step's K
+  float* v32;                 // (B*T_new, Dkv) this step's V
+  int nqb;                    // 32-row query blocks per key/value set: ceil(h/h_kv * T_new / 32)
+  int CW;                     // cached keys per split-K chunk (multiple of 64)
+  int nparts;                 // ceil(T_max / CW)
+  float* part_m;              // (B, h_kv, nqb, nparts, 32)
+  float* part_l;              // same
+  float* part_o;              // (B, h_kv, nqb, nparts, 32, d_k)
+  float* o32;                 // (B*T_new, D) attention output
+};
+// K slices (>= 1, every slice non-empty) for an M x K by K x N skinny product.
+int decode_k_split(int M, int K, int N);
+// part[ks][m][n] (KS x M x N fp32) = slice ks of X . W; X bf16 or fp32 (M x K),
+// W (K x N) bf16 row-major; K % 64 == 0, N % 8 == 0.
+hipError_t launch_rows_gemm(const void* X, bool x_f32, int M, int K, const uint16_t* W, int N,
+                            int KS, float* part, hipStream_t s);
+hipError_t launch_decode_route(const DecodeArgs& a, const float* part, int KS, hipStream_t s);
+hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t s);
+// y (M x N) fp32 = sum over KS slices of part + bias (bf16, nullable).
+hipError_t launch_decode_out(const float* part, int KS, int M, int N, const uint16_t* bias, float* y,
+                             hipStream_t s);
+
 }  // namespace mha

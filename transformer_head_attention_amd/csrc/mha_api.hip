@@ -113,6 +113,54 @@ bool sizes_ok(const mha_handle* hd, int B, int T_q, int T_k) {
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
+// Workspace of one generation step (bf16 handles).
+struct DecodeLayout {
+  size_t part = 0, q32 = 0, q16 = 0, k32 = 0, v32 = 0, o32 = 0, pm = 0, pl = 0, po = 0;
+  size_t total = 0;
+  int ks_qkv = 1, ks_out = 1, nqb = 1, CW = 64, nparts = 1;
+};
+
+bool decode_sizes_ok(int B, int T_new, int T_max) {
+  if (B < 1 || B > 65535 || T_new < 1 || T_max < T_new) return false;
+  if ((long long)B * T_new > 65535LL * 32) return false;
+  if ((long long)T_max + 256 > INT_MAX / 4) return false;
+  return true;
+}
+
+DecodeLayout make_decode_layout(const mha_handle* hd, int B, int T_new, int T_max) {
+  DecodeLayout L;
+  const size_t D = (size_t)hd->D, Dkv = (size_t)hd->Dkv, Nqkv = (size_t)hd->Nqkv;
+  const int M = B * T_new;
+  const int G = (hd->h / hd->h_kv) * T_new;
+  L.nqb = (G + 31) / 32;
+  // About 4096 waves over the whole cache capacity, chunks of whole 64-key tiles.
+  const long long cells = (long long)B * hd->h_kv * L.nqb * T_max;
+  long long cw = (cells + 4095) / 4096;
+  cw = std::max(64LL, (cw + 63) / 64 * 64);
+  L.CW = (int)std::min<long long>(cw, (long long)(T_max + 63) / 64 * 64);
+  L.nparts = (T_max + L.CW - 1) / L.CW;
+  L.ks_qkv = mha::decode_k_split(M, hd->D, hd->Nqkv);
+  L.ks_out = mha::decode_k_split(M, hd->D, hd->D);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, kAlign);
+    return at;
+  };
+  L.part = take(std::max((size_t)L.ks_qkv * M * Nqkv, (size_t)L.ks_out * M * D) * 4);
+  L.q32 = take((size_t)M * D * 4);
+  L.q16 = take((size_t)M * D * 2);
+  L.k32 = take((size_t)M * Dkv * 4);
+  L.v32 = take((size_t)M * Dkv * 4);
+  L.o32 = take((size_t)M * D * 4);
+  const size_t rows = (size_t)B * hd->h_kv * L.nqb * L.nparts * 32;
+  L.pm = take(rows * 4);
+  L.pl = take(rows * 4);
+  L.po = take(rows * hd->d_k * 4);
+  L.total = off;
+  return L;
+}
+
 #define MHA_HIP(call)                       \
   do {                                      \
     const hipError_t e_ = (call);           \
@@ -419,6 +467,87 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
                                  s));
     if (!mark(4) || !mark(5)) return MHA_ERR_HIP;
   }
+  return MHA_OK;
+}
+
+size_t mha_decode_workspace_size(mha_handle_t hd, int B, int T_new, int T_max) {
+  if (!hd || hd->dtype != MHA_BF16 || !decode_sizes_ok(B, T_new, T_max)) return 0;
+  return make_decode_layout(hd, B, T_new, T_max).total;
+}
+
+mha_status_t mha_decode(mha_handle_t hd, const void* x, const void* w_qkv, const void* b_qkv,
+                        const void* w_o, const void* b_o, int B, int T_new, void* k_cache,
+                        void* v_cache, int T_max, const int* cache_len, float* y,
+                        void* workspace, size_t workspace_bytes, void* stream_) {
+  if (!hd) return MHA_ERR_INVALID_ARG;
+  if (!x || !w_qkv || !w_o || !k_cache || !v_cache || !cache_len || !y || !workspace)
+    return MHA_ERR_INVALID_ARG;
+  if (!decode_sizes_ok(B, T_new, T_max)) return MHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w_qkv, b_qkv, w_o, b_o, k_cache, v_cache, y, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MHA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(cache_len) & 3u) != 0) return MHA_ERR_INVALID_ARG;
+  if (hd->dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
+  const DecodeLayout L = make_decode_layout(hd, B, T_new, T_max);
+  if (workspace_bytes < L.total) return MHA_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int D = hd->D, M = B * T_new;
+  hipEvent_t* ev = nullptr;
+  if (hd->prof_calls < hd->prof_max) {
+    ev = &hd->prof_ev[(size_t)hd->prof_calls * (MHA_NUM_STAGES + 1)];
+    ++hd->prof_calls;
+  }
+  auto mark = [&](int i) -> bool {
+    if (!ev) return true;
+    const hipError_t e = hipEventRecord(ev[i], s);
+    if (e != hipSuccess) g_last_hip_error = e;
+    return e == hipSuccess;
+  };
+  (void)hipGetLastError();
+  if (!mark(0) || !mark(1)) return MHA_ERR_HIP;
+
+  mha::DecodeArgs a{};
+  a.B = B;
+  a.T_new = T_new;
+  a.T_max = T_max;
+  a.D = D;
+  a.h = hd->h;
+  a.h_kv = hd->h_kv;
+  a.d_k = hd->d_k;
+  a.Dkv = hd->Dkv;
+  a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)hd->d_k));
+  a.b_qkv = static_cast<const uint16_t*>(b_qkv);
+  a.cache_len = cache_len;
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.q32 = reinterpret_cast<float*>(ws + L.q32);
+  a.q16 = reinterpret_cast<uint16_t*>(ws + L.q16);
+  a.k32 = reinterpret_cast<float*>(ws + L.k32);
+  a.v32 = reinterpret_cast<float*>(ws + L.v32);
+  a.nqb = L.nqb;
+  a.CW = L.CW;
+  a.nparts = L.nparts;
+  a.part_m = reinterpret_cast<float*>(ws + L.pm);
+  a.part_l = reinterpret_cast<float*>(ws + L.pl);
+  a.part_o = reinterpret_cast<float*>(ws + L.po);
+  a.o32 = reinterpret_cast<float*>(ws + L.o32);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+
+  // qkv_proj
+  MHA_HIP(mha::launch_rows_gemm(x, false, M, D, static_cast<const uint16_t*>(w_qkv), hd->Nqkv,
+                                L.ks_qkv, part, s));
+  MHA_HIP(mha::launch_decode_route(a, part, L.ks_qkv, s));
+  if (!mark(2)) return MHA_ERR_HIP;
+  // attention
+  MHA_HIP(mha::launch_decode_attention(a, s));
+  if (!mark(3)) return MHA_ERR_HIP;
+  // out_proj
+  MHA_HIP(mha::launch_rows_gemm(a.o32, true, M, D, static_cast<const uint16_t*>(w_o), D, L.ks_out,
+                                part, s));
+  MHA_HIP(mha::launch_decode_out(part, L.ks_out, M, D, static_cast<const uint16_t*>(b_o), y, s));
+  if (!mark(4) || !mark(5)) return MHA_ERR_HIP;
   return MHA_OK;
 }
 
