@@ -17,6 +17,11 @@ Beside the headline rate the line carries:
                 summary was taken on a different kernel source.
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of
                 the same workload (whole batch elements, about 10 s of work).
+
+Generation-step workloads (--workload decode_*): one step = one mha_decode
+call (projection of the new tokens, attention over the KV cache, output
+projection); the line reports the cache bytes read per second (value) and
+the attention stage against the HBM bandwidth (roofline bound "hbm").
 """
 
 from __future__ import annotations
@@ -110,6 +115,102 @@ def cpu_baseline(w, inp, budget_s: float = 10.0):
                       f"{flops / 1e9:.1f} GFLOP in {spent:.1f} s, fp64 numpy/BLAS"}
 
 
+def cpu_baseline_decode(w, inp, budget_s: float = 10.0):
+    """fp64 oracle generation step on whole batch elements, one after another
+    until about ``budget_s`` seconds of host work."""
+    from threadpoolctl import threadpool_info
+    from mha_inputs import as_float64_numpy as f
+    from oracle import mha_oracle
+
+    done, spent, nbytes = 0, 0.0, 0.0
+    while done < w.B and spent < budget_s:
+        b = slice(done, done + 1)
+        t0 = time.perf_counter()
+        mha_oracle.mha_decode(f(inp["x"][b]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]),
+                              f(inp["b_o"]), w.h, f(inp["k_cache"][b]), f(inp["v_cache"][b]),
+                              inp["cache_len"][b].numpy(), n_kv_heads=w.n_g)
+        spent += time.perf_counter() - t0
+        nbytes += w.cache_bytes(inp["cache_len"][b].tolist())
+        done += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences (all heads, bf16 cache upcast to fp64), "
+                      f"{nbytes / 1e6:.1f} MB of cache in {spent:.1f} s"}
+
+
+def bench_decode(args, name) -> int:
+    import torch
+    import transformer_head_attention_amd as mha
+    from mha_inputs import DECODE_WORKLOADS, make_decode_inputs
+
+    w = DECODE_WORKLOADS[name]
+    inp = make_decode_inputs(w, seed=0)
+    dev = torch.device("cuda:0")
+    t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    m = mha.MultiHeadAttention(w.D, w.h, "bf16", num_kv_heads=w.n_g)
+    y = torch.empty(w.B, w.T_new, w.D, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        # the same cache rows are rewritten every step (cache_len is not advanced)
+        m.decode(t["x"], t["w_qkv"], t["w_o"], t["k_cache"], t["v_cache"], t["cache_len"],
+                 b_qkv=t["b_qkv"], b_o=t["b_o"], out=y, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    mha._check(mha.mha_profile_begin(m.handle, args.steps), "mha_profile_begin")
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    st, stages, _ = mha.mha_profile_end(m.handle)
+    mha._check(st, "mha_profile_end")
+
+    lens = inp["cache_len"].tolist()
+    cache_bytes = w.cache_bytes(lens)
+    att_ms = stages["attention"]
+    achieved = cache_bytes / (att_ms * 1e-3) / 1e9 if att_ms > 0 else None
+    line = {
+        "metric": "MHA decode step: KV-cache bytes read per second, 1 GPU",
+        "value": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "T_new": w.T_new, "T_max": w.T_max,
+                   "cached_lengths": list(w.lengths), "D": w.D, "h": w.h, "n_kv_heads": w.n_g,
+                   "d_k": w.d_k, "cache_mb_read_per_step": round(cache_bytes / 1e6, 2),
+                   "tflops": round(w.flops(lens) / (ms * 1e-3) / 1e12, 3)},
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": None if achieved is None else round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": None if achieved is None else round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_decode(w, inp),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def copy_calibration(torch, steps: int) -> int:
     """A plain copy of known size: each launch reads and writes 1 GiB. Its
     FETCH_SIZE / WRITE_SIZE counters give the scale from counter units to
@@ -144,9 +245,11 @@ def main() -> int:
     if args.copy_calibration:
         return copy_calibration(torch, args.steps)
     import transformer_head_attention_amd as mha
-    from mha_inputs import ALL_WORKLOADS, HEADLINE, make_inputs
+    from mha_inputs import ALL_WORKLOADS, DECODE_WORKLOADS, HEADLINE, make_inputs
 
     name = args.workload or HEADLINE
+    if name in DECODE_WORKLOADS:
+        return bench_decode(args, name)
     w = ALL_WORKLOADS[name]
     inp = make_inputs(w, seed=0)
     dev = torch.device("cuda:0")

@@ -109,16 +109,13 @@ struct DecodeArgs {
   float* part_o;              // (B, h_kv, nqb, nparts, 32, d_k)
   float* o32;                 // (B*T_new, D) attention output
 };
-// K slices (>= 1, every slice non-empty) for an M x K by K x N skinny product.
-int decode_k_split(int M, int K, int N);
-// part[ks][m][n] (KS x M x N fp32) = slice ks of X . W; X bf16 or fp32 (M x K),
-// W (K x N) bf16 row-major; K % 64 == 0, N % 8 == 0.
-hipError_t launch_rows_gemm(const void* X, bool x_f32, int M, int K, const uint16_t* W, int N,
-                            int KS, float* part, hipStream_t s);
-hipError_t launch_decode_route(const DecodeArgs& a, const float* part, int KS, hipStream_t s);
-hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t s);
-// y (M x N) fp32 = sum over KS slices of part + bias (bf16, nullable).
-hipError_t launch_decode_out(const float* part, int KS, int M, int N, const uint16_t* bias, float* y,
+// [Q|K|V] of the new tokens x (B*T_new x D bf16) with W_QKV (D x N_qkv bf16,
+// row-major), routed: q32, q16, k32, v32 and the cache rows. D % 64 == 0.
+hipError_t launch_decode_qkv(const DecodeArgs& a, const uint16_t* x, const uint16_t* w_qkv,
                              hipStream_t s);
+hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t s);
+// y (M x D fp32) = o32 (M x D fp32) . W_O (D x D bf16) + bias (bf16, nullable).
+hipError_t launch_decode_out(const float* o32, int M, int D, const uint16_t* w_o,
+                             const uint16_t* bias, float* y, hipStream_t s);
 
 }  // namespace mha

@@ -115,9 +115,9 @@ thread_local hipError_t g_last_hip_error = hipSuccess;
 
 // Workspace of one generation step (bf16 handles).
 struct DecodeLayout {
-  size_t part = 0, q32 = 0, q16 = 0, k32 = 0, v32 = 0, o32 = 0, pm = 0, pl = 0, po = 0;
+  size_t q32 = 0, q16 = 0, k32 = 0, v32 = 0, o32 = 0, pm = 0, pl = 0, po = 0;
   size_t total = 0;
-  int ks_qkv = 1, ks_out = 1, nqb = 1, CW = 64, nparts = 1;
+  int nqb = 1, CW = 64, nparts = 1;
 };
 
 bool decode_sizes_ok(int B, int T_new, int T_max) {
@@ -127,27 +127,30 @@ bool decode_sizes_ok(int B, int T_new, int T_max) {
   return true;
 }
 
+// Split-K chunk width: about 2048 waves over the cache capacity, at most 32
+// chunks per query row (the merge reads every chunk), whole 64-key tiles.
+int decode_chunk(long long rows_x_keys, int T_max) {
+  long long cw = (rows_x_keys + 2047) / 2048;
+  cw = std::max<long long>(cw, ((long long)T_max + 31) / 32);
+  cw = std::max(64LL, (cw + 63) / 64 * 64);
+  return (int)std::min<long long>(cw, ((long long)T_max + 63) / 64 * 64);
+}
+
 DecodeLayout make_decode_layout(const mha_handle* hd, int B, int T_new, int T_max) {
   DecodeLayout L;
   const size_t D = (size_t)hd->D, Dkv = (size_t)hd->Dkv, Nqkv = (size_t)hd->Nqkv;
   const int M = B * T_new;
   const int G = (hd->h / hd->h_kv) * T_new;
   L.nqb = (G + 31) / 32;
-  // About 4096 waves over the whole cache capacity, chunks of whole 64-key tiles.
-  const long long cells = (long long)B * hd->h_kv * L.nqb * T_max;
-  long long cw = (cells + 4095) / 4096;
-  cw = std::max(64LL, (cw + 63) / 64 * 64);
-  L.CW = (int)std::min<long long>(cw, (long long)(T_max + 63) / 64 * 64);
+  L.CW = decode_chunk((long long)B * hd->h_kv * L.nqb * T_max, T_max);
   L.nparts = (T_max + L.CW - 1) / L.CW;
-  L.ks_qkv = mha::decode_k_split(M, hd->D, hd->Nqkv);
-  L.ks_out = mha::decode_k_split(M, hd->D, hd->D);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off = align_up(off + bytes, kAlign);
     return at;
   };
-  L.part = take(std::max((size_t)L.ks_qkv * M * Nqkv, (size_t)L.ks_out * M * D) * 4);
+  (void)Nqkv;
   L.q32 = take((size_t)M * D * 4);
   L.q16 = take((size_t)M * D * 2);
   L.k32 = take((size_t)M * Dkv * 4);
@@ -533,20 +536,17 @@ mha_status_t mha_decode(mha_handle_t hd, const void* x, const void* w_qkv, const
   a.part_l = reinterpret_cast<float*>(ws + L.pl);
   a.part_o = reinterpret_cast<float*>(ws + L.po);
   a.o32 = reinterpret_cast<float*>(ws + L.o32);
-  float* part = reinterpret_cast<float*>(ws + L.part);
 
   // qkv_proj
-  MHA_HIP(mha::launch_rows_gemm(x, false, M, D, static_cast<const uint16_t*>(w_qkv), hd->Nqkv,
-                                L.ks_qkv, part, s));
-  MHA_HIP(mha::launch_decode_route(a, part, L.ks_qkv, s));
+  MHA_HIP(mha::launch_decode_qkv(a, static_cast<const uint16_t*>(x),
+                                 static_cast<const uint16_t*>(w_qkv), s));
   if (!mark(2)) return MHA_ERR_HIP;
   // attention
   MHA_HIP(mha::launch_decode_attention(a, s));
   if (!mark(3)) return MHA_ERR_HIP;
   // out_proj
-  MHA_HIP(mha::launch_rows_gemm(a.o32, true, M, D, static_cast<const uint16_t*>(w_o), D, L.ks_out,
-                                part, s));
-  MHA_HIP(mha::launch_decode_out(part, L.ks_out, M, D, static_cast<const uint16_t*>(b_o), y, s));
+  MHA_HIP(mha::launch_decode_out(a.o32, M, D, static_cast<const uint16_t*>(w_o),
+                                 static_cast<const uint16_t*>(b_o), y, s));
   if (!mark(4) || !mark(5)) return MHA_ERR_HIP;
   return MHA_OK;
 }
