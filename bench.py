@@ -44,6 +44,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "attention": ["transformer_head_attention_amd/csrc/attn16.hip",
                   "transformer_head_attention_amd/csrc/device_common.h"],
+    "decode_attention": ["transformer_head_attention_amd/csrc/decode.hip",
+                         "transformer_head_attention_amd/csrc/device_common.h"],
 }
 
 
@@ -203,7 +205,7 @@ def bench_decode(args, name) -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": None if achieved is None else round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": read_traffic("decode_attention", name),
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_decode(w, inp),
     }
