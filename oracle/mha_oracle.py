@@ -26,6 +26,11 @@ Sources (pages as titled; sections / equations named, no line numbers):
   key/value sets, each shared by a group of query heads; the key/value
   elements per token and layer are 2 n_h d_h (MHA), 2 d_h (MQA), 2 n_g d_h
   (GQA).
+* iamjaehka13.blog §14 and §23 (shape table, residual row): the layer's
+  output can be added to its input, X' = X + O W_O (with the bias b_O, and X
+  the query-side input under cross-attention).
+* molayo1419.me, nn.MultiheadAttention's return values: the attention
+  weights, averaged over heads (N, L, S) by default or per head (N, h, L, S).
 * Same itwiki section, first paragraph, and iamjaehka13.blog §21: during
   autoregressive generation the keys and values of earlier tokens are kept in
   a KV cache, so a step computes only the new tokens' projections and reads
@@ -157,14 +162,15 @@ def _attend_grouped(qh, kh, vh, n_g, causal, mask, q_pos=None):
 
 
 def mha_forward(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
-                key_padding_mask=None, return_intermediates=False, n_kv_heads=None):
+                key_padding_mask=None, return_intermediates=False, n_kv_heads=None,
+                residual=False):
     """Y = Concat(head_1..head_h) W^O + b_O for batch-first inputs.
 
     x_q (B, T_q, D); x_kv (B, T_k, D) or None for self-attention;
     w_qkv (D, D + 2 n_g d_k) (3D wide for n_kv_heads None = h);
     b_qkv (D + 2 n_g d_k,) or None; w_o (D, D); b_o (D,) or None;
-    key_padding_mask (B, T_k), nonzero = ignore, or None.
-    Everything is evaluated in float64.
+    key_padding_mask (B, T_k), nonzero = ignore, or None. ``residual`` adds
+    x_q to the result. Everything is evaluated in float64.
     """
     x_q, x_kv, w_qkv, b_qkv, w_o, b_o = map(_as64, (x_q, x_kv, w_qkv, b_qkv, w_o, b_o))
     B, T_q, D = x_q.shape
@@ -179,13 +185,28 @@ def mha_forward(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
     o, a = _attend_grouped(qh, kh, vh, n_g, causal, key_padding_mask)
     o_cat = concat_heads(o)
     y = linear(o_cat, w_o, b_o)
+    if residual:
+        y = x_q + y
     if return_intermediates:
         return y, {"q": qh, "k": kh, "v": vh, "a": a, "o": o_cat}
     return y
 
 
+def attention_weights(x_q, w_qkv, b_qkv, h, x_kv=None, causal=False, key_padding_mask=None,
+                      n_kv_heads=None, average=False):
+    """The softmax weights A of every head, (B, h, T_q, T_k), or their mean
+    over heads, (B, T_q, T_k), for the same inputs as ``mha_forward``."""
+    x_q, x_kv, w_qkv, b_qkv = map(_as64, (x_q, x_kv, w_qkv, b_qkv))
+    D = x_q.shape[2]
+    n_g = _kv_width(w_qkv, D, h, n_kv_heads)
+    q, k, v = _qkv(x_q, x_kv, w_qkv, b_qkv, D)
+    _, a = _attend_grouped(split_heads(q, h), split_heads(k, n_g), split_heads(v, n_g), n_g,
+                           causal, key_padding_mask)
+    return a.mean(axis=1) if average else a
+
+
 def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
-                     causal=False, key_padding_mask=None, n_kv_heads=None):
+                     causal=False, key_padding_mask=None, n_kv_heads=None, residual=False):
     """Y[b, t, :] for selected query rows only.
 
     ``rows`` maps a batch index b to a 1-D array of query positions t. The
@@ -213,6 +234,8 @@ def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
         kh, vh = split_heads(k, n_g), split_heads(v, n_g)
         o, _ = _attend_grouped(qh, kh, vh, n_g, causal, mask_b, q_pos=ts)
         out[b] = linear(concat_heads(o), w_o, b_o)[0]
+        if residual:
+            out[b] = xq_b[0] + out[b]
     return out
 
 
