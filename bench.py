@@ -235,6 +235,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--residual", action="store_true", help="y = x_q + attention output")
+    ap.add_argument("--y-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (HBM counter scale)")
     args = ap.parse_args()
@@ -258,13 +260,14 @@ def main() -> int:
     t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     m = mha.MultiHeadAttention(w.D, w.h, w.dtype, num_kv_heads=w.n_g)
     ws = m.workspace(w.B, w.T_q, w.T_k, dev)
-    y = torch.empty(w.B, w.T_q, w.D, dtype=torch.float32, device=dev)
+    ydt = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
+    y = torch.empty(w.B, w.T_q, w.D, dtype=ydt, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
         m.forward(t["x_q"], t["w_qkv"], t["w_o"], b_qkv=t["b_qkv"], b_o=t["b_o"], x_kv=t["x_kv"],
                   causal=w.causal, key_padding_mask=t["key_padding_mask"], out=y, workspace=ws,
-                  stream=stream.cuda_stream)
+                  stream=stream.cuda_stream, residual=args.residual, y_dtype=args.y_dtype)
 
     # Untimed warmup: the first few hundred microseconds of sustained work
     # run at a different clock than the steady state that follows.
@@ -315,7 +318,8 @@ def main() -> int:
         "config": {"workload": name, "B": w.B, "T_q": w.T_q, "T_k": w.T_k, "D": w.D, "h": w.h,
                    "n_kv_heads": w.n_g, "d_k": w.d_k, "causal": w.causal, "cross": w.cross,
                    "key_padding": w.padding is not None, "gflop_per_step": round(flops / 1e9, 3),
-                   "intermediates": "fp16 Q/K/V/P/O, fp32 accumulate, fp32 Y"},
+                   "intermediates": "fp16 Q/K/V/P/O, fp32 accumulate",
+                   "y": args.y_dtype, "residual": args.residual},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_MFMA_16BIT_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": {

@@ -164,6 +164,43 @@ mha_status_t mha_decode(mha_handle_t handle, const void* x,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* ---- Output options of the forward pass ----------------------------------
+ * residual         1: y = x_q + MultiHead(...) (iamjaehka13.blog "[Deep
+ *                  Learning 5]", §14 and the residual row of its §23 table:
+ *                  the layer output is added to the query-side input).
+ * y_bf16           1: y is stored as bf16 (round to nearest even) instead of
+ *                  fp32; MHA_BF16 handles only (MHA_ERR_UNSUPPORTED otherwise).
+ * attn_weights     NULL, or a DEVICE buffer, 16-byte aligned, receiving the
+ *                  softmax weights as nn.MultiheadAttention returns them
+ *                  (molayo1419.me, return values): per head (B, h, T_q, T_k)
+ *                  fp32, or with average_weights = 1 their mean over heads
+ *                  (B, T_q, T_k). Masked keys get weight 0; a row whose keys
+ *                  are all masked is NaN. Inspection output for small
+ *                  problems: T_k <= 4096 and B <= 65535, else
+ *                  MHA_ERR_UNSUPPORTED. On the bf16 path the weights come
+ *                  from the fp16 Q and K of the computation (relative error
+ *                  about 1e-3), on the fp32 path from fp32 Q and K. Recorded
+ *                  in the "attention" stage of the timing hooks. */
+typedef struct {
+  int residual;
+  int y_bf16;
+  float* attn_weights;
+  int average_weights;
+} mha_forward_options;
+
+/* mha_forward with options (opts may be NULL: the defaults, all zero, are
+ * exactly mha_forward). y is (B, T_q, D) fp32, or bf16 with opts->y_bf16. */
+mha_status_t mha_forward_ex(mha_handle_t handle,
+                            const void* x_q, const void* x_kv,
+                            const void* w_qkv, const void* b_qkv,
+                            const void* w_o, const void* b_o,
+                            int B, int T_q, int T_k, int causal,
+                            const unsigned char* key_padding_mask,
+                            void* y,
+                            void* workspace, size_t workspace_bytes,
+                            const mha_forward_options* opts,
+                            void* stream);
+
 /* Release a handle (NULL is accepted). */
 mha_status_t mha_destroy(mha_handle_t handle);
 

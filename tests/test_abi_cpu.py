@@ -184,3 +184,28 @@ def test_decode_validation_without_device_work(mha):
     finally:
         mha.mha_destroy(h)
         mha.mha_destroy(h32)
+
+
+def test_forward_options_validation(mha):
+    st, h = mha.mha_create(512, 8, mha.MHA_BF16)
+    st2, h32 = mha.mha_create(512, 8, mha.MHA_F32)
+    fake = 1 << 20
+    try:
+        ws = mha.mha_workspace_size(h, 2, 16, 16)
+
+        def call(opts, handle=h, T=16):
+            return mha.mha_forward_ex(handle, fake, None, fake, None, fake, None, 2, T, T, 0,
+                                      None, fake, fake, mha.mha_workspace_size(handle, 2, T, T),
+                                      opts, None)
+
+        O = mha.mha_forward_options
+        assert call(O(2, 0, None, 0)) == mha.MHA_ERR_INVALID_ARG      # residual not 0/1
+        assert call(O(0, 3, None, 0)) == mha.MHA_ERR_INVALID_ARG
+        assert call(O(0, 0, fake + 4, 0)) == mha.MHA_ERR_INVALID_ARG  # misaligned weights
+        assert call(O(0, 1, None, 0), handle=h32) == mha.MHA_ERR_UNSUPPORTED   # bf16 y, fp32 path
+        assert call(O(0, 0, fake, 0), T=5000) == mha.MHA_ERR_UNSUPPORTED        # weights, T_k > 4096
+        assert mha.mha_forward_ex(h, None, None, fake, None, fake, None, 2, 16, 16, 0, None, fake,
+                                  fake, ws, O(1, 0, None, 0), None) == mha.MHA_ERR_INVALID_ARG
+    finally:
+        mha.mha_destroy(h)
+        mha.mha_destroy(h32)

@@ -33,7 +33,8 @@ MHA_F32, MHA_BF16 = 0, 1
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP = range(5)
 MHA_NUM_STAGES = 5
 
-EXPORTED = ("mha_create", "mha_create_grouped", "mha_workspace_size", "mha_forward", "mha_destroy",
+EXPORTED = ("mha_create", "mha_create_grouped", "mha_workspace_size", "mha_forward",
+            "mha_forward_ex", "mha_destroy",
             "mha_decode_workspace_size", "mha_decode",
             "mha_status_string", "mha_hip_error_string", "mha_profile_begin", "mha_profile_end",
             "mha_stage_name")
@@ -48,6 +49,16 @@ _lib.mha_workspace_size.restype = _sz
 _lib.mha_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
                              _vp, _vp, _sz, _vp]
 _lib.mha_forward.restype = _int
+
+
+class mha_forward_options(ctypes.Structure):
+    _fields_ = [("residual", ctypes.c_int), ("y_bf16", ctypes.c_int),
+                ("attn_weights", ctypes.c_void_p), ("average_weights", ctypes.c_int)]
+
+
+_lib.mha_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
+                                _vp, _vp, _sz, ctypes.POINTER(mha_forward_options), _vp]
+_lib.mha_forward_ex.restype = _int
 _lib.mha_decode_workspace_size.argtypes = [_vp, _int, _int, _int]
 _lib.mha_decode_workspace_size.restype = _sz
 _lib.mha_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _vp, _vp, _int, _vp, _vp,
@@ -135,6 +146,15 @@ def mha_decode(handle, x, w_qkv, b_qkv, w_o, b_o, B, T_new, k_cache, v_cache, T_
                            stream)
 
 
+def mha_forward_ex(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k, causal,
+                   key_padding_mask, y, workspace, workspace_bytes, opts, stream) -> int:
+    """Raw call; ``opts`` is an mha_forward_options or None."""
+    return _lib.mha_forward_ex(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, int(B), int(T_q),
+                               int(T_k), int(causal), key_padding_mask, y, workspace,
+                               int(workspace_bytes), None if opts is None else ctypes.byref(opts),
+                               stream)
+
+
 def mha_destroy(handle) -> int:
     return _lib.mha_destroy(handle)
 
@@ -220,15 +240,24 @@ class MultiHeadAttention:
                 raise ValueError(f"expected shape {shape}, got {tuple(t.shape)}")
 
     def forward(self, x_q, w_qkv, w_o, b_qkv=None, b_o=None, x_kv=None, causal=False,
-                key_padding_mask=None, out=None, workspace=None, stream=None):
+                key_padding_mask=None, out=None, workspace=None, stream=None, residual=False,
+                y_dtype="fp32", attn_weights=None, average_weights=False):
+        """Returns y. ``residual`` adds x_q; ``y_dtype`` "bf16" stores y as
+        bf16; ``attn_weights`` (a (B, h, T_q, T_k) fp32 tensor, or (B, T_q,
+        T_k) with ``average_weights``) receives the softmax weights."""
         torch = self._torch
         if x_q.dim() != 3:
             raise ValueError("x_q must be (B, T, D)")
         self._check_shapes(x_q, w_qkv, w_o, b_qkv, b_o, x_kv, key_padding_mask, out)
         B, T_q, D = x_q.shape
         T_k = T_q if x_kv is None else x_kv.shape[1]
+        ydt = {"fp32": torch.float32, "bf16": torch.bfloat16}[y_dtype]
         if out is None:
-            out = torch.empty(B, T_q, D, dtype=torch.float32, device=x_q.device)
+            out = torch.empty(B, T_q, D, dtype=ydt, device=x_q.device)
+        if attn_weights is not None:
+            want = (B, T_q, T_k) if average_weights else (B, self.num_heads, T_q, T_k)
+            if tuple(attn_weights.shape) != want:
+                raise ValueError(f"attn_weights must be {want}")
         if workspace is None:
             workspace = self.workspace(B, T_q, T_k, x_q.device)
         if key_padding_mask is not None and key_padding_mask.dtype != torch.uint8:
@@ -236,12 +265,19 @@ class MultiHeadAttention:
         if stream is None:
             stream = torch.cuda.current_stream(x_q.device).cuda_stream
         dt = self._tdtype
-        st = mha_forward(self.handle, self._ptr(x_q, dt), self._ptr(x_kv, dt),
-                         self._ptr(w_qkv, dt), self._ptr(b_qkv, dt), self._ptr(w_o, dt),
-                         self._ptr(b_o, dt), B, T_q, T_k, 1 if causal else 0,
-                         self._ptr(key_padding_mask), self._ptr(out, torch.float32),
-                         workspace.data_ptr(), workspace.numel(), stream)
-        _check(st, "mha_forward")
+        args = (self.handle, self._ptr(x_q, dt), self._ptr(x_kv, dt), self._ptr(w_qkv, dt),
+                self._ptr(b_qkv, dt), self._ptr(w_o, dt), self._ptr(b_o, dt), B, T_q, T_k,
+                1 if causal else 0, self._ptr(key_padding_mask), self._ptr(out, ydt),
+                workspace.data_ptr(), workspace.numel())
+        if not residual and y_dtype == "fp32" and attn_weights is None:
+            st = mha_forward(*args, stream)
+            _check(st, "mha_forward")
+        else:
+            opts = mha_forward_options(1 if residual else 0, 1 if y_dtype == "bf16" else 0,
+                                       self._ptr(attn_weights, torch.float32),
+                                       1 if average_weights else 0)
+            st = mha_forward_ex(*args, opts, stream)
+            _check(st, "mha_forward_ex")
         return out
 
     __call__ = forward

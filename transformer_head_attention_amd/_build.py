@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "libmha")
 LIB = os.path.join(PKG, "libmha.so")
 
-SOURCES = ["mha_api.hip", "prep.hip", "gemm16.hip", "attn16.hip", "fp32_path.hip", "decode.hip"]
+SOURCES = ["mha_api.hip", "prep.hip", "gemm16.hip", "attn16.hip", "fp32_path.hip", "decode.hip",
+           "weights.hip"]
 
 # Per-source extra flags. The attention kernel keeps its MFMA accumulators in
 # ordinary VGPRs (no AGPR copies around the softmax); the large GEMM tiles need

@@ -34,14 +34,6 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// Two fp32 -> packed bf16x2 (low half = a), round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t h = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
-  return __builtin_bit_cast(uint32_t, h);
-}
-
 // Eight bf16 values -> eight fp16 values (exact for normal-range values).
 __device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& r) {
   u32x4 o;

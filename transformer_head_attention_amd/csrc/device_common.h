@@ -81,6 +81,15 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even (gfx950
+// converts in hardware).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t h = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 __device__ __forceinline__ float f16_bits_to_float(uint16_t v) {
   return static_cast<float>(__builtin_bit_cast(_Float16, v));
 }

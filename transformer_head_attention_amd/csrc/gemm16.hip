@@ -484,9 +484,11 @@ struct VEpi {
 // fp32 result epilogue of the output projection, on transposed tiles: a lane
 // holds row m and four consecutive columns n..n+3 per fragment group, which
 // go out as one 16-byte store (four stores cover a 128-byte line of a row).
+template <bool RESID, bool YBF16>
 struct OutEpi {
   const uint16_t* bias;
-  float* Y;
+  void* Y;               // fp32, or bf16 with YBF16
+  const uint16_t* resid; // (M x N) bf16 added to the result with RESID
   template <int TM, int TN>
   __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
                                         int M, int N, uint8_t* /*lds*/) const {
@@ -510,7 +512,16 @@ struct OutEpi {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = mbase + i * 32 + lq;
-      float* yr = Y + (size_t)m * N + nbase;
+      // The row's residual values, fetched together (rows past M read row M-1).
+      u32x2 rr[TN][4];
+      if constexpr (RESID) {
+        const uint16_t* xr = resid + (size_t)min(m, M - 1) * N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg)
+            rr[j][rg] = *reinterpret_cast<const u32x2*>(xr + min(nbase + j * 32 + 8 * rg + 4 * lh, N - 4));
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -518,11 +529,24 @@ struct OutEpi {
           const int c = j * 32 + 8 * rg + 4 * lh;
           const f32x16_t& a = acc[i][j];
           const u32x2 b2 = bb[j][rg];
-          const f32x4_t v = {a[rg * 4 + 0] + __uint_as_float(b2.x << 16),
-                             a[rg * 4 + 1] + __uint_as_float(b2.x & 0xffff0000u),
-                             a[rg * 4 + 2] + __uint_as_float(b2.y << 16),
-                             a[rg * 4 + 3] + __uint_as_float(b2.y & 0xffff0000u)};
-          if (full || (m < M && nbase + c < N)) *reinterpret_cast<f32x4_t*>(yr + c) = v;
+          f32x4_t v = {a[rg * 4 + 0] + __uint_as_float(b2.x << 16),
+                       a[rg * 4 + 1] + __uint_as_float(b2.x & 0xffff0000u),
+                       a[rg * 4 + 2] + __uint_as_float(b2.y << 16),
+                       a[rg * 4 + 3] + __uint_as_float(b2.y & 0xffff0000u)};
+          if constexpr (RESID) {
+            const u32x2 r2 = rr[j][rg];
+            v[0] += __uint_as_float(r2.x << 16);
+            v[1] += __uint_as_float(r2.x & 0xffff0000u);
+            v[2] += __uint_as_float(r2.y << 16);
+            v[3] += __uint_as_float(r2.y & 0xffff0000u);
+          }
+          if (full || (m < M && nbase + c < N)) {
+            if constexpr (YBF16)
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Y) + (size_t)m * N + nbase + c) =
+                  u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            else
+              *reinterpret_cast<f32x4_t*>(static_cast<float*>(Y) + (size_t)m * N + nbase + c) = v;
+          }
         }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -540,7 +564,7 @@ constexpr int EO_WAVES = 4;
 
 __global__ void __launch_bounds__(EO_WAVES * 64)
 early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __restrict__ WoT,
-                 int N, const uint16_t* __restrict__ bias, float* __restrict__ Y, int R, int T_q) {
+                 int N, const uint16_t* __restrict__ bias, OutOptions opt, int R, int T_q) {
   __shared__ f32x16_t red[EO_WAVES - 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
@@ -598,7 +622,13 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
     const int m = m0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     if (m < M) {
       const int bb = m / R, t = m - bb * R;
-      Y[((size_t)bb * T_q + t) * N + n] = acc[r] + bv;
+      const size_t yi = ((size_t)bb * T_q + t) * N + n;
+      float v = acc[r] + bv;
+      if (opt.resid) v += bf16_bits_to_float(opt.resid[yi]);
+      if (opt.y_bf16)
+        static_cast<uint16_t*>(opt.y)[yi] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
+      else
+        static_cast<float*>(opt.y)[yi] = v;
     }
   }
 }
@@ -672,23 +702,37 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
 }
 
 hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
-                            const uint16_t* bias, float* Y, int R, int T_q, hipStream_t s) {
+                            const uint16_t* bias, const OutOptions& opt, int R, int T_q,
+                            hipStream_t s) {
   dim3 grid(N / 32, (M + 31) / 32);
-  hipLaunchKernelGGL(early_out_kernel, grid, dim3(EO_WAVES * 64), 0, s, O32, M, K, WoT, N, bias, Y, R,
-                     T_q);
+  hipLaunchKernelGGL(early_out_kernel, grid, dim3(EO_WAVES * 64), 0, s, O32, M, K, WoT, N, bias, opt,
+                     R, T_q);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_out(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
-                           const uint16_t* bias, float* Y, hipStream_t s) {
-  OutEpi epi{bias, Y};
+namespace {
+template <bool RESID, bool YBF16>
+hipError_t launch_out_variant(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
+                              const uint16_t* bias, const OutOptions& opt, hipStream_t s) {
+  OutEpi<RESID, YBF16> epi{bias, opt.y, opt.resid};
   if (use_big(M, N))
-    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi>), dim3(tiles_of(M, N, 256, 256)),
-                       dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
+    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>>),
+                       dim3(tiles_of(M, N, 256, 256)), dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
   else
-    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, true, OutEpi>), dim3(tiles_of(M, N, 128, 128)),
-                       dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K, epi);
+    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, true, OutEpi<RESID, YBF16>>),
+                       dim3(tiles_of(M, N, 128, 128)), dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K, epi);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_out(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
+                           const uint16_t* bias, const OutOptions& opt, hipStream_t s) {
+  if (opt.resid) {
+    if (opt.y_bf16) return launch_out_variant<true, true>(A, M, K, Bt, N, bias, opt, s);
+    return launch_out_variant<true, false>(A, M, K, Bt, N, bias, opt, s);
+  }
+  if (opt.y_bf16) return launch_out_variant<false, true>(A, M, K, Bt, N, bias, opt, s);
+  return launch_out_variant<false, false>(A, M, K, Bt, N, bias, opt, s);
 }
 
 }  // namespace mha

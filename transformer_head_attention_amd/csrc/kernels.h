@@ -41,14 +41,21 @@ struct QkvEpilogue {
 // A: (M x K) bf16, Bt: (N x K) bf16.
 hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
                            const QkvEpilogue& e, hipStream_t s);
-// A: (M x K) fp16, Bt: (N x K) fp16; Y (M x N) fp32 = A . Bt^T + bias (bf16, nullable).
+// Where and how the output projection stores Y.
+struct OutOptions {
+  void* y;                // (M x N) fp32, or bf16 (round to nearest even) with y_bf16
+  int y_bf16;
+  const uint16_t* resid;  // (M x N) bf16 added to Y (the query-side input), or null
+};
+// A: (M x K) fp16, Bt: (N x K) fp16; Y (M x N) = A . Bt^T + bias (bf16, nullable) [+ resid].
 hipError_t launch_gemm_out(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
-                           const uint16_t* bias, float* Y, hipStream_t s);
+                           const uint16_t* bias, const OutOptions& opt, hipStream_t s);
 
-// Early causal rows: Y[b*T_q + t] = O32[b*R + t] . W_O + bias for t < R, from
+// Early causal rows: Y[b*T_q + t] = O32[b*R + t] . W_O + bias [+ resid] for t < R, from
 // fp32 O32 (M = B*R rows x K) and fp16 W_O^T (N x K); N % 32 == 0, K % 64 == 0.
 hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
-                            const uint16_t* bias, float* Y, int R, int T_q, hipStream_t s);
+                            const uint16_t* bias, const OutOptions& opt, int R, int T_q,
+                            hipStream_t s);
 
 // ---- fused attention, fp16 operands, fp32 softmax state ------------------
 struct AttnF16Args {
@@ -86,6 +93,25 @@ struct AttnF32Args {
   int B, h, rows, T_k, causal;                 // rows = query rows evaluated (t = 0..rows-1)
 };
 hipError_t launch_attn_f32(const AttnF32Args& a, int d_k, hipStream_t s);
+// y[i] += x[i] for i < n (fp32).
+hipError_t launch_add_residual_f32(float* y, const float* x, size_t n, hipStream_t s);
+
+// ---- attention weights (inspection output) --------------------------------
+// A[b][head][t][j] (or the mean over heads) = softmax over keys j of
+// score_scale * (q . k), masked like the attention (causal, padding, j < T_k).
+// q row (b, head, t) at q + b*q_bs + head*q_hs + t*q_ld; k row (b, set, j) at
+// k + b*k_bs + set*k_hs + j*k_ld, set = head / group. Elements fp16 (F16) or fp32.
+struct WeightsArgs {
+  const void* q; long q_bs, q_hs; int q_ld;
+  const void* k; long k_bs, k_hs; int k_ld;
+  int f16;                     // element type of q and k
+  float score_scale;           // multiplies q . k; scores are then in log2 units
+  const uint8_t* mask;         // (B, T_k) nonzero = ignore, or null
+  int B, h, group, T_q, T_k, d_k, causal, average;
+  float* out;                  // (B, h, T_q, T_k) or, with average, (B, T_q, T_k)
+};
+hipError_t launch_attn_weights(const WeightsArgs& a, hipStream_t s);
+constexpr int kWeightsMaxKeys = 4096;
 // rows <= T_k <= 64 (the first rows of causal sequences).
 hipError_t launch_attn_early(const AttnF32Args& a, int d_k, hipStream_t s);
 

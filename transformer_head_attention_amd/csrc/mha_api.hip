@@ -278,8 +278,27 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
                          const void* b_qkv, const void* w_o, const void* b_o, int B, int T_q,
                          int T_k, int causal, const unsigned char* key_padding_mask, float* y,
                          void* workspace, size_t workspace_bytes, void* stream_) {
+  return mha_forward_ex(hd, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k, causal,
+                        key_padding_mask, y, workspace, workspace_bytes, nullptr, stream_);
+}
+
+mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, const void* w_qkv,
+                            const void* b_qkv, const void* w_o, const void* b_o, int B, int T_q,
+                            int T_k, int causal, const unsigned char* key_padding_mask, void* y,
+                            void* workspace, size_t workspace_bytes,
+                            const mha_forward_options* opts, void* stream_) {
   if (!hd) return MHA_ERR_INVALID_ARG;
   if (!x_q || !w_qkv || !w_o || !y || !workspace) return MHA_ERR_INVALID_ARG;
+  const int residual = opts ? opts->residual : 0;
+  const int y_bf16 = opts ? opts->y_bf16 : 0;
+  float* weights = opts ? opts->attn_weights : nullptr;
+  const int average = opts ? opts->average_weights : 0;
+  if ((residual != 0 && residual != 1) || (y_bf16 != 0 && y_bf16 != 1) ||
+      (average != 0 && average != 1))
+    return MHA_ERR_INVALID_ARG;
+  if (weights && !aligned16(weights)) return MHA_ERR_INVALID_ARG;
+  if (y_bf16 && hd->dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
+  if (weights && (T_k > mha::kWeightsMaxKeys || B > 65535)) return MHA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return MHA_ERR_INVALID_ARG;
   if (!x_kv && T_k != T_q) return MHA_ERR_INVALID_ARG;
   if (causal && T_k != T_q) return MHA_ERR_INVALID_ARG;
@@ -295,6 +314,17 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
   const int D = hd->D, h = hd->h, d_k = hd->d_k, h_kv = hd->h_kv, Dkv = hd->Dkv,
             Nqkv = hd->Nqkv;
   const bool cross = x_kv != nullptr;
+  mha::WeightsArgs wa{};
+  wa.mask = key_padding_mask;
+  wa.B = B;
+  wa.h = h;
+  wa.group = h / h_kv;
+  wa.T_q = T_q;
+  wa.T_k = T_k;
+  wa.d_k = d_k;
+  wa.causal = causal;
+  wa.average = average;
+  wa.out = weights;
 
   // stage boundary events (measurement only)
   hipEvent_t* ev = nullptr;
@@ -389,10 +419,24 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     a.D = D;
     a.causal = causal;
     MHA_HIP(mha::launch_attn_f16(a, d_k, s));
+    if (weights) {
+      wa.q = q;
+      wa.q_hs = (long)L.Tqp * d_k;
+      wa.q_bs = wa.q_hs * h;
+      wa.q_ld = d_k;
+      wa.k = k;
+      wa.k_hs = (long)L.Tkp * d_k;
+      wa.k_bs = wa.k_hs * h_kv;
+      wa.k_ld = d_k;
+      wa.f16 = 1;
+      wa.score_scale = 1.0f;   // Q already carries log2(e)/sqrt(d_k)
+      MHA_HIP(mha::launch_attn_weights(wa, s));
+    }
     if (!mark(3)) return MHA_ERR_HIP;
 
     // out_proj
-    MHA_HIP(mha::launch_gemm_out(o, B * T_q, D, woT, D, static_cast<const uint16_t*>(b_o), y, s));
+    mha::OutOptions oo{y, y_bf16, residual ? xq : nullptr};
+    MHA_HIP(mha::launch_gemm_out(o, B * T_q, D, woT, D, static_cast<const uint16_t*>(b_o), oo, s));
     if (!mark(4)) return MHA_ERR_HIP;
 
     // early_rows
@@ -415,7 +459,7 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
       f.T_k = L.R;
       f.causal = 1;
       MHA_HIP(mha::launch_attn_early(f, d_k, s));
-      MHA_HIP(mha::launch_early_out(eo, B * L.R, D, woT, D, static_cast<const uint16_t*>(b_o), y,
+      MHA_HIP(mha::launch_early_out(eo, B * L.R, D, woT, D, static_cast<const uint16_t*>(b_o), oo,
                                     L.R, T_q, s));
     }
     if (!mark(5)) return MHA_ERR_HIP;
@@ -465,9 +509,24 @@ mha_status_t mha_forward(mha_handle_t hd, const void* x_q, const void* x_kv, con
     f.T_k = T_k;
     f.causal = causal;
     MHA_HIP(mha::launch_attn_f32(f, d_k, s));
+    if (weights) {
+      wa.q = f.q;
+      wa.q_bs = f.q_bstride;
+      wa.q_hs = d_k;
+      wa.q_ld = f.q_ld;
+      wa.k = f.k;
+      wa.k_bs = f.kv_bstride;
+      wa.k_hs = d_k;
+      wa.k_ld = f.kv_ld;
+      wa.f16 = 0;
+      wa.score_scale = (float)(1.4426950408889634 / std::sqrt((double)d_k));
+      MHA_HIP(mha::launch_attn_weights(wa, s));
+    }
     if (!mark(3)) return MHA_ERR_HIP;
-    MHA_HIP(mha::launch_gemm_f32(fo, D, B * T_q, D, w_o, D, D, false, b_o, y, D, B * T_q, B * T_q,
+    float* yf = static_cast<float*>(y);
+    MHA_HIP(mha::launch_gemm_f32(fo, D, B * T_q, D, w_o, D, D, false, b_o, yf, D, B * T_q, B * T_q,
                                  s));
+    if (residual) MHA_HIP(mha::launch_add_residual_f32(yf, xq, (size_t)B * T_q * D, s));
     if (!mark(4) || !mark(5)) return MHA_ERR_HIP;
   }
   return MHA_OK;
