@@ -78,8 +78,11 @@ __device__ __forceinline__ int swz(int row, int c) {
   return CHUNKS == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ (row & 15));
 }
 
+// d_k = 128: the register budget is capped at two waves per SIMD (a few
+// registers spill); with two pipeline stages (64 KiB of LDS) two workgroups
+// then share a CU, which is faster than one unspilled workgroup.
 template <int DK, int NQ, int NS, bool HAS_MASK>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT, (DK == 128 ? 2 : 1))
 attn_f16_kernel(AttnF16Args a) {
   constexpr int BLOCK_M = NWAVES * 32 * NQ;
   constexpr int KCH = DK / 8;                       // 16-byte chunks per K row
@@ -368,7 +371,7 @@ attn_f16_kernel(AttnF16Args a) {
 #define MHA_ATTN_NS64 3
 #endif
 #ifndef MHA_ATTN_NS128
-#define MHA_ATTN_NS128 3
+#define MHA_ATTN_NS128 2
 #endif
 constexpr int nq_for(int d_k) { return d_k == 64 ? MHA_ATTN_NQ64 : 1; }
 
