@@ -496,6 +496,7 @@ hipError_t launch_decode_qkv(const DecodeArgs& a, const uint16_t* x, const uint1
 
 hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t s) {
   if (a.h_kv < 1 || a.h % a.h_kv != 0 || a.CW % 64 != 0 || a.CW < 64) return hipErrorInvalidValue;
+  if (a.h > 65535 || (long long)a.h_kv * a.nqb > 65535 || a.B > 65535) return hipErrorInvalidValue;
   dim3 g1(a.nparts, a.h_kv * a.nqb, a.B);
   dim3 g2(a.T_new, a.h, a.B);
   if (a.d_k == 64) {
