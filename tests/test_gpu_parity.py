@@ -129,6 +129,13 @@ MID = [
     ("bf16 MQA causal d_k=128 T=129", W["causal_bf16_d4096_h32_b1_t8192"],
      dict(D=1024, h=8, T_q=129, T_k=129, n_kv=1)),
     ("bf16 GQA T=1 causal", W["causal_bf16_d512_h8_b16_t1024"], dict(B=3, T_q=1, T_k=1, n_kv=2)),
+    # causal cross-attention (T_q == T_k): early rows take Q from x_q, K and V from x_kv
+    ("bf16 causal cross padded", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
+     dict(B=3, T_q=150, T_k=150, causal=True, padding=(100, 150))),
+    ("bf16 causal cross GQA d_k=128", W["causal_bf16_d4096_h32_b1_t8192"],
+     dict(D=1024, h=8, B=2, T_q=140, T_k=140, cross=True, n_kv=2)),
+    ("fp32 causal cross", W["self_fp32_d512_h8_b2_t128"],
+     dict(T_q=90, T_k=90, cross=True, causal=True)),
     ("fp32 GQA g2 causal ragged", W["self_fp32_d512_h8_b2_t128"],
      dict(T_q=201, T_k=201, causal=True, n_kv=2)),
     ("fp32 MQA cross padded", W["self_fp32_d512_h8_b2_t128"],
