@@ -557,35 +557,44 @@ struct OutEpi {
 // fp32 attention output: Y[b*T_q + t] = O32[b*R + t] . W_O + b_O for t < R.
 // Each fp32 value x is split into fp16 hi = fp16(x) and lo = fp16(x - hi), and
 // hi . W + lo . W is accumulated in fp32 on the fp16 MFMA, which keeps about
-// 22 significant bits of x. A workgroup owns a 32 x 32 tile of Y; its four
-// waves take a quarter of K each (loads issued in batches of k-steps, each
-// batch before its MFMAs) and are summed through LDS in a fixed order.
+// 22 significant bits of x. A workgroup owns a 32 x (32 EO_TN) tile of Y (the
+// O rows it loads serve EO_TN column blocks); its four waves take a quarter
+// of K each (loads issued in batches of k-steps, each batch before its
+// MFMAs) and are summed through LDS in a fixed order.
 constexpr int EO_WAVES = 4;
+#ifndef MHA_EO_TN
+#define MHA_EO_TN 2
+#endif
+constexpr int EO_TN = MHA_EO_TN;
 
 __global__ void __launch_bounds__(EO_WAVES * 64)
 early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __restrict__ WoT,
                  int N, const uint16_t* __restrict__ bias, OutOptions opt, int R, int T_q) {
-  __shared__ f32x16_t red[EO_WAVES - 1][64];
+  __shared__ f32x16_t red[EO_WAVES - 1][EO_TN][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32 * EO_TN;
   const int kw = K / EO_WAVES, kbeg = wave * kw;
   const int row = min(m0 + (lane & 31), M - 1);
   const float* ap = O32 + (size_t)row * K + (lane >> 5) * 8;
   const uint16_t* bp = WoT + (size_t)(n0 + (lane & 31)) * K + (lane >> 5) * 8;
-  f32x16_t acc;
+  f32x16_t acc[EO_TN];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int j = 0; j < EO_TN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
   // NB k-steps at a time: all of their loads go out before the first MFMA,
   // so a batch costs one memory latency.
   auto batch = [&](auto nb_tag, int k) __attribute__((always_inline)) {
     constexpr int NB = decltype(nb_tag)::value;
     f32x4_t a0[NB], a1[NB];
-    u32x4 bf[NB];
+    u32x4 bf[NB][EO_TN];
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       a0[s] = *reinterpret_cast<const f32x4_t*>(ap + k + 16 * s);
       a1[s] = *reinterpret_cast<const f32x4_t*>(ap + k + 16 * s + 4);
-      bf[s] = *reinterpret_cast<const u32x4*>(bp + k + 16 * s);
+#pragma unroll
+      for (int j = 0; j < EO_TN; ++j)
+        bf[s][j] = *reinterpret_cast<const u32x4*>(bp + (size_t)j * 32 * K + k + 16 * s);
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -599,8 +608,12 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
         hi[e] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
         lo[e] = pack_f16x2(av[2 * e] - static_cast<float>(h0), av[2 * e + 1] - static_cast<float>(h1));
       }
-      acc = mfma32x32x16<F16>(u32x4{hi[0], hi[1], hi[2], hi[3]}, bf[s], acc);
-      acc = mfma32x32x16<F16>(u32x4{lo[0], lo[1], lo[2], lo[3]}, bf[s], acc);
+      const u32x4 ah = u32x4{hi[0], hi[1], hi[2], hi[3]}, al = u32x4{lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+      for (int j = 0; j < EO_TN; ++j) {
+        acc[j] = mfma32x32x16<F16>(ah, bf[s][j], acc[j]);
+        acc[j] = mfma32x32x16<F16>(al, bf[s][j], acc[j]);
+      }
     }
   };
   int k = kbeg;
@@ -610,25 +623,30 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
     k += 16 * 4;
   }
   for (; k < kbeg + kw; k += 16) batch(std::integral_constant<int, 1>{}, k);
-  if (wave > 0) red[wave - 1][lane] = acc;
+  if (wave > 0)
+#pragma unroll
+    for (int j = 0; j < EO_TN; ++j) red[wave - 1][j][lane] = acc[j];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 0; w < EO_WAVES - 1; ++w) acc += red[w][lane];
-  const int n = n0 + (lane & 31);
-  const float bv = load_bias_bf16(bias, n);
+  for (int j = 0; j < EO_TN; ++j) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (m < M) {
-      const int bb = m / R, t = m - bb * R;
-      const size_t yi = ((size_t)bb * T_q + t) * N + n;
-      float v = acc[r] + bv;
-      if (opt.resid) v += bf16_bits_to_float(opt.resid[yi]);
-      if (opt.y_bf16)
-        static_cast<uint16_t*>(opt.y)[yi] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
-      else
-        static_cast<float*>(opt.y)[yi] = v;
+    for (int w = 0; w < EO_WAVES - 1; ++w) acc[j] += red[w][j][lane];
+    const int n = n0 + 32 * j + (lane & 31);
+    const float bv = load_bias_bf16(bias, n);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (m < M) {
+        const int bb = m / R, t = m - bb * R;
+        const size_t yi = ((size_t)bb * T_q + t) * N + n;
+        float v = acc[j][r] + bv;
+        if (opt.resid) v += bf16_bits_to_float(opt.resid[yi]);
+        if (opt.y_bf16)
+          static_cast<uint16_t*>(opt.y)[yi] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
+        else
+          static_cast<float*>(opt.y)[yi] = v;
+      }
     }
   }
 }
@@ -704,7 +722,8 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
 hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
                             const uint16_t* bias, const OutOptions& opt, int R, int T_q,
                             hipStream_t s) {
-  dim3 grid(N / 32, (M + 31) / 32);
+  if (N % (32 * EO_TN) != 0 || K % (16 * EO_WAVES) != 0) return hipErrorInvalidValue;
+  dim3 grid(N / (32 * EO_TN), (M + 31) / 32);
   hipLaunchKernelGGL(early_out_kernel, grid, dim3(EO_WAVES * 64), 0, s, O32, M, K, WoT, N, bias, opt,
                      R, T_q);
   return hipGetLastError();
