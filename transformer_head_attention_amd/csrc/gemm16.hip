@@ -706,9 +706,21 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
   // transposed tiles, the V part with normal tiles.
   const int n_lo = e.n_base, n_hi = e.n_base + N, split = e.D + e.Dkv;
   if (n_lo < split) {
+    // With grouped key/value heads the K block is narrower than Q: Q and K
+    // run as separate launches so that each picks its own tile size (one
+    // launch over D + Dkv columns would leave a mostly empty last round of
+    // large tiles).
+    const int cut = (e.Dkv < e.D && n_lo < e.D && min(n_hi, split) > e.D) ? e.D : min(n_hi, split);
     QkEpi epi{e};
-    const hipError_t err = launch_qkv_part<true>(A, M, K, Bt, min(n_hi, split) - n_lo, epi, s);
+    hipError_t err = launch_qkv_part<true>(A, M, K, Bt, cut - n_lo, epi, s);
     if (err != hipSuccess) return err;
+    if (cut < min(n_hi, split)) {
+      QkEpi epi_k{e};
+      epi_k.e.n_base = cut;
+      err = launch_qkv_part<true>(A, M, K, Bt + (size_t)(cut - n_lo) * K, min(n_hi, split) - cut,
+                                  epi_k, s);
+      if (err != hipSuccess) return err;
+    }
   }
   if (n_hi > split) {
     const int v_lo = max(n_lo, split);
