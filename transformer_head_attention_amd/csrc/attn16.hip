@@ -78,12 +78,119 @@ __device__ __forceinline__ int swz(int row, int c) {
   return CHUNKS == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ (row & 15));
 }
 
+// ---------------------------------------------------------------------------
+// Early causal rows in fp32. Query rows t < rows of every causal sequence see
+// at most 64 keys, so their outputs are averages of few value rows and are
+// the largest of the layer; they are evaluated a second time here from the
+// fp32 Q/K/V the QKV epilogue saved, and their output projection
+// (early_out_kernel) later overwrites those rows of Y. The workgroups doing
+// this come first in the attention grid (their count rounded up to a
+// multiple of 8, so the attention blocks keep their XCD placement); being
+// short, they leave room to the long causal blocks within microseconds,
+// which is cheaper than a launch of their own. A workgroup takes 16 query rows of one (batch, head); 16
+// lanes share a row, each owning d_k/16 dimensions; all (<= 64) keys of the
+// row sit in LDS as fp32 (rows past the extent zeroed, so the key loops have
+// no branches), the scores in registers: two plain passes (maximum, then
+// exponentials and the weighted sum of V), in log2 units.
+constexpr int ER = 16;   // query rows per early-row workgroup
+
+// Sum over the 16 lanes of a DPP row (every lane gets the total):
+// quad_perm xor 1, quad_perm xor 2, row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+long long early_blocks(const AttnF32Args& e) {
+  return (long long)((e.rows + ER - 1) / ER) * e.h * e.B;
+}
+
+// blk: (row block, head, batch element) of the early rows; lds: at least
+// 2 * 64 * DK * 4 bytes.
+template <int DK>
+__device__ __forceinline__ void early_rows_block(const AttnF32Args& a, int blk, uint8_t* lds) {
+  constexpr int CPL = DK / 16;   // dimensions per lane
+  float (*Ks)[DK] = reinterpret_cast<float (*)[DK]>(lds);
+  float (*Vs)[DK] = reinterpret_cast<float (*)[DK]>(lds + 64 * DK * 4);
+  const int nx = (a.rows + ER - 1) / ER;
+  const int bx = blk % nx, head = (blk / nx) % a.h, b = blk / (nx * a.h);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = lane & 15;
+  const int t = bx * ER + wave * 4 + (lane >> 4);
+  const bool valid = t < a.rows;
+  const int kend = a.causal ? min(a.T_k, bx * ER + ER) : a.T_k;   // <= 64 (host-checked)
+
+  const float* kb = a.k + (size_t)b * a.kv_bstride + (head / a.group) * DK;
+  const float* vb = a.v + (size_t)b * a.kv_bstride + (head / a.group) * DK;
+  for (int idx = tid; idx < 64 * (DK / 4); idx += NT) {
+    const int key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
+    f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
+    if (key < kend) {
+      kv = *reinterpret_cast<const f32x4_t*>(kb + (size_t)key * a.kv_ld + c4);
+      vv = *reinterpret_cast<const f32x4_t*>(vb + (size_t)key * a.kv_ld + c4);
+    }
+    *reinterpret_cast<f32x4_t*>(&Ks[key][c4]) = kv;
+    *reinterpret_cast<f32x4_t*>(&Vs[key][c4]) = vv;
+  }
+  // Keys this row ignores: past the extent, in the future, or padded.
+  const bool padded = a.mask && lane < kend && a.mask[(size_t)b * a.mask_ld + lane] != 0;
+  const uint64_t padm = __ballot(padded);
+
+  // q pre-multiplied by log2(e) / sqrt(d_k): the softmax is exp2(s - max).
+  const float scale = 1.4426950408889634f / sqrtf((float)DK);
+  float q[CPL];
+  const float* qp = a.q + (size_t)b * a.q_bstride + (size_t)(valid ? t : 0) * a.q_ld + head * DK +
+                    p * CPL;
+#pragma unroll
+  for (int c = 0; c < CPL; c += 4) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(qp + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[c + e] = v[e] * scale;
+  }
+  __syncthreads();
+  const int seen_keys = a.causal ? min(kend, t + 1) : kend;
+  const uint64_t live = (seen_keys >= 64 ? ~0ull : ((1ull << max(seen_keys, 0)) - 1)) & ~padm;
+
+  float sc[64];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    float part = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) part = __builtin_fmaf(q[c], Ks[j][p * CPL + c], part);
+    part = row16_sum(part);
+    sc[j] = ((live >> j) & 1ull) ? part : -INFINITY;
+    mx = fmaxf(mx, sc[j]);
+  }
+  const float base = mx == -INFINITY ? 0.0f : mx;
+  float l = 0.0f, o[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) o[c] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const float pj = __builtin_amdgcn_exp2f(sc[j] - base);
+    l += pj;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[c] = __builtin_fmaf(pj, Vs[j][p * CPL + c], o[c]);
+  }
+  if (valid) {
+    float* op = a.o + (size_t)b * a.o_bstride + (size_t)t * a.o_ld + head * DK + p * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; c += 4)
+      *reinterpret_cast<f32x4_t*>(op + c) =
+          f32x4_t{o[c] / l, o[c + 1] / l, o[c + 2] / l, o[c + 3] / l};
+  }
+}
+
 // d_k = 128: the register budget is capped at two waves per SIMD (a few
 // registers spill); with two pipeline stages (64 KiB of LDS) two workgroups
 // then share a CU, which is faster than one unspilled workgroup.
 template <int DK, int NQ, int NS, bool HAS_MASK>
 __global__ void __launch_bounds__(NT, (DK == 128 ? 2 : 1))
-attn_f16_kernel(AttnF16Args a) {
+attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   constexpr int BLOCK_M = NWAVES * 32 * NQ;
   constexpr int KCH = DK / 8;                       // 16-byte chunks per K row
   constexpr int K_BYTES = BLOCK_N * DK * 2;
@@ -98,6 +205,13 @@ attn_f16_kernel(AttnF16Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
   __shared__ __attribute__((aligned(16))) uint32_t mask_s[NS][2];
 
+  // The first early_slots workgroups evaluate the early causal rows.
+  if ((int)blockIdx.x < early_slots) {
+    static_assert(NS * STAGE >= 2 * 64 * DK * 4, "early-row staging fits the stages");
+    if ((long long)blockIdx.x < (long long)((early.rows + ER - 1) / ER) * early.h * early.B)
+      early_rows_block<DK>(early, (int)blockIdx.x, smem);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 31, lh = lane >> 5;
 
@@ -105,7 +219,7 @@ attn_f16_kernel(AttnF16Args a) {
   // (batch, head) run on one XCD and share its L2 copy of K and V; under the
   // causal mask the longest blocks are dispatched first.
   const int nqb = a.Tqp / BLOCK_M;
-  const int logical = xcd_remap(blockIdx.x, nqb * a.h * a.B);
+  const int logical = xcd_remap((int)blockIdx.x - early_slots, nqb * a.h * a.B);
   const int bh = logical / nqb;
   int qblk = logical - bh * nqb;
   if (a.causal) qblk = nqb - 1 - qblk;
@@ -376,12 +490,14 @@ attn_f16_kernel(AttnF16Args a) {
 constexpr int nq_for(int d_k) { return d_k == 64 ? MHA_ATTN_NQ64 : 1; }
 
 template <int DK, int NS>
-hipError_t launch_dk(const AttnF16Args& a, int total, hipStream_t s) {
+hipError_t launch_dk(const AttnF16Args& a, int total, const AttnF32Args& e, int extra,
+                     hipStream_t s) {
   if (a.mbits)
-    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, true>), dim3(total), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, true>), dim3(total + extra), dim3(NT),
+                       0, s, a, e, extra);
   else
-    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, false>), dim3(total), dim3(NT), 0, s,
-                       a);
+    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, false>), dim3(total + extra),
+                       dim3(NT), 0, s, a, e, extra);
   return hipGetLastError();
 }
 
@@ -416,12 +532,26 @@ hipError_t launch_mask_bits(const uint8_t* mask, int B, int T_k, uint32_t* bits,
   return hipGetLastError();
 }
 
-hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, hipStream_t s) {
+hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* early,
+                           hipStream_t s) {
   if (a.h_kv < 1 || a.h % a.h_kv != 0) return hipErrorInvalidValue;
+  AttnF32Args e{};
+  int extra = 0;
+  if (early) {
+    // rows <= T_k <= 64 (the early rows of causal sequences)
+    if (early->T_k < 1 || early->T_k > 64 || early->rows > early->T_k || early->group < 1 ||
+        early->h % early->group != 0)
+      return hipErrorInvalidValue;
+    e = *early;
+    const long long n = (early_blocks(e) + 7) / 8 * 8;
+    if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+    extra = (int)n;
+  }
   const int bm = attn_f16_block_m(d_k);
   const int total = (a.Tqp / bm) * a.h * a.B;
-  if (d_k == 64) return launch_dk<64, MHA_ATTN_NS64>(a, total, s);
-  if (d_k == 128) return launch_dk<128, MHA_ATTN_NS128>(a, total, s);
+  if ((long long)total + extra > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (d_k == 64) return launch_dk<64, MHA_ATTN_NS64>(a, total, e, extra, s);
+  if (d_k == 128) return launch_dk<128, MHA_ATTN_NS128>(a, total, e, extra, s);
   return hipErrorInvalidValue;
 }
 

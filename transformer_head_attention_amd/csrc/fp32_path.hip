@@ -1,5 +1,4 @@
-// fp32 kernels: the whole path for fp32 inputs, and the re-evaluation of the
-// first rows of each causal sequence for bf16 inputs.
+// fp32 kernels: the whole path for fp32 inputs.
 //
 //  * gemm_f32: C = A . B + bias with v_mfma_f32_16x16x4_f32 (full fp32
 //    products and sums); B and bias may be stored as bf16 (converted exactly).
@@ -10,8 +9,6 @@
 //    query row is shared by d_k/16 lanes that each own 16 of its dimensions;
 //    keys are staged through LDS in chunks of 64 and folded into a running
 //    max / running sum.
-//  * attn_early: the same for the first (at most 64) rows of causal
-//    sequences, whose keys all fit in LDS at once.
 #include <math.h>
 
 #include "device_common.h"
@@ -185,104 +182,6 @@ attn_f32_kernel(AttnF32Args a) {
   }
 }
 
-// Sum over the 16 lanes of a DPP row (every lane gets the total):
-// quad_perm xor 1, quad_perm xor 2, row_half_mirror, row_mirror.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-  return v;
-}
-
-// attn_early: the same row softmax for short key ranges (at most 64 keys, the
-// first rows of a causal sequence). A workgroup takes 16 query rows of one
-// (batch, head); 16 lanes share a row, each owning d_k/16 dimensions. All of
-// the row's scores stay in registers, so the softmax is two plain passes
-// (maximum, then exponentials and the weighted sum of V).
-constexpr int ER = 16;   // query rows per workgroup
-
-template <int DK>
-__global__ void __launch_bounds__(256)
-attn_early_kernel(AttnF32Args a) {
-  constexpr int CPL = DK / 16;   // dimensions per lane
-  __shared__ __attribute__((aligned(16))) float Ks[64][DK];
-  __shared__ __attribute__((aligned(16))) float Vs[64][DK];
-  __shared__ uint8_t Ms[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int p = lane & 15;
-  const int head = blockIdx.y, b = blockIdx.z;
-  const int t = blockIdx.x * ER + wave * 4 + (lane >> 4);
-  const bool valid = t < a.rows;
-  const int kend = a.causal ? min(a.T_k, blockIdx.x * ER + ER) : a.T_k;   // <= 64 (host-checked)
-
-  // Keys [0, kend) of this head; rows past kend are zero so that the key
-  // loops below can run over all 64 rows without branches (their weights
-  // are exactly 0 and 0 * 0 stays 0).
-  const float* kb = a.k + (size_t)b * a.kv_bstride + (head / a.group) * DK;
-  const float* vb = a.v + (size_t)b * a.kv_bstride + (head / a.group) * DK;
-  for (int idx = tid; idx < 64 * (DK / 4); idx += 256) {
-    const int key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
-    f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
-    if (key < kend) {
-      kv = *reinterpret_cast<const f32x4_t*>(kb + (size_t)key * a.kv_ld + c4);
-      vv = *reinterpret_cast<const f32x4_t*>(vb + (size_t)key * a.kv_ld + c4);
-    }
-    *reinterpret_cast<f32x4_t*>(&Ks[key][c4]) = kv;
-    *reinterpret_cast<f32x4_t*>(&Vs[key][c4]) = vv;
-  }
-  if (tid < 64) Ms[tid] = (a.mask && tid < kend) ? a.mask[(size_t)b * a.mask_ld + tid] : 0;
-
-  // Scores in log2 units: q is pre-multiplied by log2(e) / sqrt(d_k), so the
-  // softmax is exp2(s - max) (the same weights as exp(qk/sqrt(d_k) - max)).
-  const float scale = 1.4426950408889634f / sqrtf((float)DK);
-  float q[CPL];
-  const float* qp = a.q + (size_t)b * a.q_bstride + (size_t)(valid ? t : 0) * a.q_ld + head * DK +
-                    p * CPL;
-#pragma unroll
-  for (int c = 0; c < CPL; c += 4) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(qp + c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) q[c + e] = v[e] * scale;
-  }
-  __syncthreads();
-  // Ignored keys of this row as a bitmask: past the extent, in the future
-  // (causal) or flagged in the padding mask.
-  const uint64_t padm = __ballot(Ms[lane] != 0);
-  const int seen_keys = a.causal ? min(kend, t + 1) : kend;
-  const uint64_t live = (seen_keys >= 64 ? ~0ull : ((1ull << max(seen_keys, 0)) - 1)) & ~padm;
-
-  float sc[64];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    float part = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) part = __builtin_fmaf(q[c], Ks[j][p * CPL + c], part);
-    part = row16_sum(part);
-    sc[j] = ((live >> j) & 1ull) ? part : -INFINITY;
-    mx = fmaxf(mx, sc[j]);
-  }
-  const float base = mx == -INFINITY ? 0.0f : mx;
-  float l = 0.0f, o[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) o[c] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    const float pj = __builtin_amdgcn_exp2f(sc[j] - base);
-    l += pj;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) o[c] = __builtin_fmaf(pj, Vs[j][p * CPL + c], o[c]);
-  }
-  if (valid) {
-    float* op = a.o + (size_t)b * a.o_bstride + (size_t)t * a.o_ld + head * DK + p * CPL;
-#pragma unroll
-    for (int c = 0; c < CPL; c += 4)
-      *reinterpret_cast<f32x4_t*>(op + c) =
-          f32x4_t{o[c] / l, o[c + 1] / l, o[c + 2] / l, o[c + 3] / l};
-  }
-}
-
 }  // namespace
 
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B, int ldb, int N,
@@ -295,19 +194,6 @@ hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B,
   else
     hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, dim3(256), 0, s, A, lda, M, K, B, ldb, N,
                        bias, C, ldc, rows_in, rows_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_early(const AttnF32Args& a, int d_k, hipStream_t s) {
-  if (a.T_k < 1 || a.T_k > 64 || a.rows > a.T_k) return hipErrorInvalidValue;
-  if (a.group < 1 || a.h % a.group != 0) return hipErrorInvalidValue;
-  dim3 grid((a.rows + ER - 1) / ER, a.h, a.B);
-  if (d_k == 64)
-    hipLaunchKernelGGL(attn_early_kernel<64>, grid, dim3(256), 0, s, a);
-  else if (d_k == 128)
-    hipLaunchKernelGGL(attn_early_kernel<128>, grid, dim3(256), 0, s, a);
-  else
-    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -72,7 +72,11 @@ int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp, Tkp must be m
 int attn_mask_tiles(int T_k);    // 64-key tiles covering T_k
 // bits[b][tile] (two uint32): bit j set if key tile*64+j is masked or >= T_k.
 hipError_t launch_mask_bits(const uint8_t* mask, int B, int T_k, uint32_t* bits, hipStream_t s);
-hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, hipStream_t s);
+// early (nullable): the fp32 early causal rows (rows <= T_k <= 64), evaluated
+// by extra workgroups at the start of the same launch.
+struct AttnF32Args;
+hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* early,
+                           hipStream_t s);
 
 // ---- fp32 path -----------------------------------------------------------
 // C[map(m)][n] = sum_k A[m][k] * B[k][n] + bias[n], with
@@ -112,8 +116,6 @@ struct WeightsArgs {
 };
 hipError_t launch_attn_weights(const WeightsArgs& a, hipStream_t s);
 constexpr int kWeightsMaxKeys = 4096;
-// rows <= T_k <= 64 (the first rows of causal sequences).
-hipError_t launch_attn_early(const AttnF32Args& a, int d_k, hipStream_t s);
 
 // ---- generation step against a KV cache (bf16 handles) ------------------
 struct DecodeArgs {

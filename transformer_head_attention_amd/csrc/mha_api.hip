@@ -418,7 +418,28 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     a.Tkp = L.Tkp;
     a.D = D;
     a.causal = causal;
-    MHA_HIP(mha::launch_attn_f16(a, d_k, s));
+    // Early causal rows, re-evaluated in fp32 by workgroups appended to the
+    // attention launch (their output projection follows out_proj).
+    mha::AttnF32Args f{};
+    if (causal) {
+      f.q = eqkv;
+      f.k = eqkv + D;
+      f.v = eqkv + D + Dkv;
+      f.q_ld = f.kv_ld = Nqkv;
+      f.q_bstride = f.kv_bstride = (long)L.R * Nqkv;
+      f.group = h / h_kv;
+      f.o = eo;
+      f.o_ld = D;
+      f.o_bstride = (long)L.R * D;
+      f.mask = key_padding_mask;
+      f.mask_ld = T_k;
+      f.B = B;
+      f.h = h;
+      f.rows = L.R;
+      f.T_k = L.R;
+      f.causal = 1;
+    }
+    MHA_HIP(mha::launch_attn_f16(a, d_k, causal ? &f : nullptr, s));
     if (weights) {
       wa.q = q;
       wa.q_hs = (long)L.Tqp * d_k;
@@ -441,24 +462,6 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
 
     // early_rows
     if (causal) {
-      mha::AttnF32Args f{};
-      f.q = eqkv;
-      f.k = eqkv + D;
-      f.v = eqkv + D + Dkv;
-      f.q_ld = f.kv_ld = Nqkv;
-      f.q_bstride = f.kv_bstride = (long)L.R * Nqkv;
-      f.group = h / h_kv;
-      f.o = eo;
-      f.o_ld = D;
-      f.o_bstride = (long)L.R * D;
-      f.mask = key_padding_mask;
-      f.mask_ld = T_k;
-      f.B = B;
-      f.h = h;
-      f.rows = L.R;
-      f.T_k = L.R;
-      f.causal = 1;
-      MHA_HIP(mha::launch_attn_early(f, d_k, s));
       MHA_HIP(mha::launch_early_out(eo, B * L.R, D, woT, D, static_cast<const uint16_t*>(b_o), oo,
                                     L.R, T_q, s));
     }
