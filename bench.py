@@ -17,6 +17,12 @@ Beside the headline rate the line carries:
                 summary was taken on a different kernel source.
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of
                 the same workload (whole batch elements, about 10 s of work).
+  step_ms       median and minimum of single steps (a further pass, one
+                event pair per step).
+  flushed       the same per-step times with 512 MiB written between steps
+                (inputs and weights evicted from L2 and the Infinity Cache).
+  peak_device   the dense 16-bit MFMA peak recomputed from the device's CU
+                count and peak clock (4096 flop per clock per CU).
 
 Generation-step workloads (--workload decode_*): one step = one mha_decode
 call (projection of the new tokens, attention over the KV cache, output
@@ -88,6 +94,53 @@ def read_traffic(stage: str, workload: str):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def step_times(torch, stream, step, n: int, flush_bytes: int = 0):
+    """Sorted single-step times (ms): one event pair per step on the launch
+    stream. With flush_bytes, a buffer of that size is overwritten before each
+    step, outside its events."""
+    buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0") if flush_bytes else None
+    evs = []
+    for i in range(n):
+        if buf is not None:
+            buf.fill_(i & 0xff)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in evs)
+
+
+def median(v):
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def device_peak():
+    """Dense 16-bit MFMA peak from the device's CU count and peak clock, read
+    with hipDeviceGetAttribute from the HIP runtime already in the process."""
+    import ctypes
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    if path is None:
+        return None
+    hip = ctypes.CDLL(path)
+    clock_khz, cus = ctypes.c_int(0), ctypes.c_int(0)
+    # hipDeviceAttributeClockRate = 5, hipDeviceAttributeMultiprocessorCount = 63
+    if hip.hipDeviceGetAttribute(ctypes.byref(clock_khz), 5, 0) != 0:
+        return None
+    if hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, 0) != 0:
+        return None
+    tflops = cus.value * clock_khz.value * 1e3 * 4096 / 1e12
+    return {"cus": cus.value, "clock_mhz": clock_khz.value / 1e3, "tflops": round(tflops, 1)}
 
 
 def cpu_baseline(w, inp, budget_s: float = 10.0):
@@ -297,6 +350,8 @@ def main() -> int:
     mha._check(st, "mha_profile_end")
 
     flops = w.flops()
+    single = step_times(torch, stream, step, args.steps)
+    flushed = step_times(torch, stream, step, args.steps, flush_bytes=512 << 20)
     tflops = flops / (ms * 1e-3) / 1e12
     dom = max(("qkv_proj", "attention", "out_proj"), key=lambda s: stages[s])
     dom_ms = stages[dom]
@@ -322,6 +377,11 @@ def main() -> int:
                    "y": args.y_dtype, "residual": args.residual},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_MFMA_16BIT_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "step_ms": {"median": round(median(single), 4), "min": round(single[0], 4)},
+        "flushed": {"median_ms": round(median(flushed), 4), "min_ms": round(flushed[0], 4),
+                    "value_median": round(flops / (median(flushed) * 1e-3) / 1e12, 2),
+                    "flush_bytes": 512 << 20},
+        "peak_device": device_peak(),
         "roofline": {
             "kernel": dom,
             "bound": "mfma",

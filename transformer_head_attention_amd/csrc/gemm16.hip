@@ -28,10 +28,11 @@ namespace mha {
 namespace gemm_impl {
 
 // BM x BN output tile, WM x WN per wave, BK-deep K slices (32 or 64 16-bit
-// elements: 64- or 128-byte LDS rows), NS slices in flight.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
+// elements: 64- or 128-byte LDS rows), NS slices in flight, OCC waves per
+// SIMD (the register budget: 512 / OCC per lane, accumulators included).
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int OCC_ = 1>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, OCC = OCC_;
   static constexpr int CH = BK / 8;                 // 16-byte chunks per LDS row
   static constexpr int WAVES_N = BN / WN;
   static constexpr int NWAVES = (BM / WM) * WAVES_N;
@@ -102,7 +103,7 @@ __device__ __forceinline__ void sched_run() {
 // per lane, one row m and four consecutive columns n (instead of one column
 // and four consecutive rows).
 template <typename C, typename Tag, bool TRANS, typename Epi>
-__global__ void __launch_bounds__(C::NT)
+__global__ void __launch_bounds__(C::NT, C::OCC)
 gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, int M, int N,
               int K, Epi epi) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NS * C::STAGE];
@@ -673,7 +674,9 @@ int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + 
 #ifndef MHA_GEMM_BIG_MIN_TILES
 #define MHA_GEMM_BIG_MIN_TILES 384
 #endif
-bool use_big(int M, int N) { return tiles_of(M, N, 256, 256) >= MHA_GEMM_BIG_MIN_TILES; }
+bool use_big(int M, int N) {
+  return tiles_of(M, N, BigCfg::BM, BigCfg::BN) >= MHA_GEMM_BIG_MIN_TILES;
+}
 
 }  // namespace gemm_impl
 
@@ -689,13 +692,15 @@ hipError_t launch_qkv_part(const uint16_t* A, int M, int K, const uint16_t* Bt, 
   if constexpr (TRANS) big = use_big(M, N);
   if constexpr (TRANS) {
     if (big) {
-      hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi>), dim3(tiles_of(M, N, 256, 256)),
-                         dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
+      hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi>),
+                         dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
+                         Bt, M, N, K, epi);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi>), dim3(tiles_of(M, N, 128, 128)),
-                     dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K, epi);
+  hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi>),
+                     dim3(tiles_of(M, N, SmallCfg::BM, SmallCfg::BN)), dim3(SmallCfg::NT), 0, s, A,
+                     Bt, M, N, K, epi);
   return hipGetLastError();
 }
 }  // namespace
@@ -748,10 +753,12 @@ hipError_t launch_out_variant(const uint16_t* A, int M, int K, const uint16_t* B
   OutEpi<RESID, YBF16> epi{bias, opt.y, opt.resid};
   if (use_big(M, N))
     hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>>),
-                       dim3(tiles_of(M, N, 256, 256)), dim3(BigCfg::NT), 0, s, A, Bt, M, N, K, epi);
+                       dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
+                       Bt, M, N, K, epi);
   else
     hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, true, OutEpi<RESID, YBF16>>),
-                       dim3(tiles_of(M, N, 128, 128)), dim3(SmallCfg::NT), 0, s, A, Bt, M, N, K, epi);
+                       dim3(tiles_of(M, N, SmallCfg::BM, SmallCfg::BN)), dim3(SmallCfg::NT), 0,
+                       s, A, Bt, M, N, K, epi);
   return hipGetLastError();
 }
 }  // namespace
