@@ -404,17 +404,21 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
           }
       }
 
-      // Row maximum as four independent chains (short dependency depth).
-      float m4[4];
+      // Row maximum: two chains of three-input maxima over the 32 scores.
+      // (vmax3 is inline assembly, before which the compiler inserts no wait
+      // states; the V^T fragment reads pinned after the score MFMAs and the
+      // mask branch put well over the 11 that a VALU read of an 8-pass MFMA
+      // result needs between the two.)
+      float m2[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16_t& sv = s[qi][g >> 1];
-        const int r0 = (g & 1) * 8;
-        m4[g] = fmaxf(fmaxf(fmaxf(sv[r0], sv[r0 + 1]), fmaxf(sv[r0 + 2], sv[r0 + 3])),
-                      fmaxf(fmaxf(sv[r0 + 4], sv[r0 + 5]), fmaxf(sv[r0 + 6], sv[r0 + 7])));
+      for (int g = 0; g < 2; ++g) {
+        const f32x16_t& sv = s[qi][g];
+        float m = vmax3(sv[0], sv[1], sv[2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) m = vmax3(m, sv[r], sv[r + 1]);
+        m2[g] = vmax2(m, sv[15]);
       }
-      float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-      mx = pair32_max(mx);
+      float mx = pair32_max(vmax2(m2[0], m2[1]));
       const bool first = !seen[qi] && mx != -INFINITY;
       const float shift = first ? mx : (mx > 8.0f ? mx : 0.0f);
       if (__ballot(shift != 0.0f)) {

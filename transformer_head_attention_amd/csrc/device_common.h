@@ -101,13 +101,28 @@ __device__ __forceinline__ float load_bias_bf16(const uint16_t* b, int i) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Maximum of three / two floats as one v_max3_f32 / v_max_f32. fmaxf on
+// values the compiler cannot prove canonical (MFMA results) first
+// canonicalizes each input with an extra v_max_f32 x, x; these take the
+// values as they are (inputs here are never signaling NaNs).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: a VALU
 // exchange of the two lane halves, no LDS round trip). Swapping v with itself
 // leaves each lane's own value in one result and its partner's in the other.
 __device__ __forceinline__ float pair32_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
