@@ -212,7 +212,10 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       early_rows_block<DK>(early, (int)blockIdx.x, smem);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index in a scalar register: the query rows of the wave, the DMA LDS
+  // bases and the causal tests on them stay scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, lh = lane >> 5;
 
   // Workgroup -> (batch, head, query block). All query blocks of one
