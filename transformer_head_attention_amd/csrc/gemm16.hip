@@ -558,49 +558,83 @@ struct OutEpi {
 // fp32 attention output: Y[b*T_q + t] = O32[b*R + t] . W_O + b_O for t < R.
 // Each fp32 value x is split into fp16 hi = fp16(x) and lo = fp16(x - hi), and
 // hi . W + lo . W is accumulated in fp32 on the fp16 MFMA, which keeps about
-// 22 significant bits of x. A workgroup owns a 32 x (32 EO_TN) tile of Y (the
-// O rows it loads serve EO_TN column blocks); its four waves take a quarter
-// of K each (loads issued in batches of k-steps, each batch before its
-// MFMAs) and are summed through LDS in a fixed order.
+// 22 significant bits of x. A workgroup owns a 32 x 64 tile of Y. K is cut
+// into 64-deep chunks dealt round-robin to the four waves; each wave copies
+// its chunks of O (32 rows, fp32) and of W_O^T (64 columns, fp16) global ->
+// LDS itself (1 KiB contiguous per instruction, two chunks in flight, no
+// workgroup barrier), reads its MFMA fragments from there, and the four
+// partial tiles are summed through LDS in a fixed order.
 constexpr int EO_WAVES = 4;
-#ifndef MHA_EO_TN
-#define MHA_EO_TN 2
-#endif
-constexpr int EO_TN = MHA_EO_TN;
+constexpr int EO_TN = 2;                          // 32-column blocks per tile
+constexpr int EO_KC = 64;                         // K per chunk
+constexpr int EO_A_BYTES = 32 * EO_KC * 4;        // 8 KiB: 32 rows x 64 fp32
+constexpr int EO_B_BYTES = 32 * EO_TN * EO_KC * 2;   // 8 KiB: 64 columns x 64 fp16
+constexpr int EO_STAGE = EO_A_BYTES + EO_B_BYTES;
 
 __global__ void __launch_bounds__(EO_WAVES * 64)
 early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __restrict__ WoT,
                  int N, const uint16_t* __restrict__ bias, OutOptions opt, int R, int T_q) {
-  __shared__ f32x16_t red[EO_WAVES - 1][EO_TN][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[EO_WAVES * 2 * EO_STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32 * EO_TN;
-  const int kw = K / EO_WAVES, kbeg = wave * kw;
-  const int row = min(m0 + (lane & 31), M - 1);
-  const float* ap = O32 + (size_t)row * K + (lane >> 5) * 8;
-  const uint16_t* bp = WoT + (size_t)(n0 + (lane & 31)) * K + (lane >> 5) * 8;
+  const int lq = lane & 31, lh = lane >> 5;
+  uint8_t* const wbase = smem + wave * 2 * EO_STAGE;
+
+  // Chunk `c` into stage `st`. LDS rows: A 256 bytes (16 chunks of 16 B,
+  // chunk index XOR row & 15), B 128 bytes (8 chunks, XOR (row >> 1) & 7), so
+  // the fragment reads below are free of bank conflicts; lane p of each
+  // instruction lands at byte 16 p of a 1 KiB window and fetches the global
+  // chunk that the swizzle places there. Rows past M are clamped (never
+  // stored).
+  auto issue = [&](int c, int st) __attribute__((always_inline)) {
+    const int k0 = c * EO_KC;
+    uint8_t* as = wbase + st * EO_STAGE;
+    uint8_t* bs = as + EO_A_BYTES;
+#pragma unroll
+    for (int i = 0; i < EO_A_BYTES / 1024; ++i) {
+      const int slot = i * 64 + lane, row = slot >> 4, ch = (slot & 15) ^ (row & 15);
+      lds_dma16(O32 + (size_t)min(m0 + row, M - 1) * K + k0 + ch * 4, as + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < EO_B_BYTES / 1024; ++i) {
+      const int slot = i * 64 + lane, row = slot >> 3, ch = (slot & 7) ^ ((row >> 1) & 7);
+      lds_dma16(WoT + (size_t)(n0 + row) * K + k0 + ch * 8, bs + i * 1024);
+    }
+  };
+  constexpr int LPC = (EO_A_BYTES + EO_B_BYTES) / 1024;   // DMA instructions per chunk
+
   f32x16_t acc[EO_TN];
 #pragma unroll
   for (int j = 0; j < EO_TN; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-  // NB k-steps at a time: all of their loads go out before the first MFMA,
-  // so a batch costs one memory latency.
-  auto batch = [&](auto nb_tag, int k) __attribute__((always_inline)) {
-    constexpr int NB = decltype(nb_tag)::value;
-    f32x4_t a0[NB], a1[NB];
-    u32x4 bf[NB][EO_TN];
+
+  const int nch = K / EO_KC;
+  // this wave's chunks: wave, wave + 4, ...
+  const int mine = nch > wave ? (nch - wave + EO_WAVES - 1) / EO_WAVES : 0;
+  if (mine > 0) issue(wave, 0);
+  if (mine > 1) issue(wave + EO_WAVES, 1);
+  for (int i = 0; i < mine; ++i) {
+    if (i + 1 < mine) wait_vmcnt<LPC>();
+    else wait_vmcnt<0>();
+    const uint8_t* as = wbase + (i & 1) * EO_STAGE;
+    const uint8_t* bs = as + EO_A_BYTES;
 #pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      a0[s] = *reinterpret_cast<const f32x4_t*>(ap + k + 16 * s);
-      a1[s] = *reinterpret_cast<const f32x4_t*>(ap + k + 16 * s + 4);
+    for (int ks = 0; ks < EO_KC / 16; ++ks) {
+      // A: this lane's 8 k-values of row lq are logical chunks 4 ks + 2 lh, +1.
+      const int c0 = 4 * ks + 2 * lh;
+      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(as + lq * 256 + ((c0 ^ (lq & 15)) << 4));
+      const f32x4_t a1 =
+          *reinterpret_cast<const f32x4_t*>(as + lq * 256 + (((c0 + 1) ^ (lq & 15)) << 4));
+      u32x4 bf[EO_TN];
 #pragma unroll
-      for (int j = 0; j < EO_TN; ++j)
-        bf[s][j] = *reinterpret_cast<const u32x4*>(bp + (size_t)j * 32 * K + k + 16 * s);
-    }
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      const float av[8] = {a0[s][0], a0[s][1], a0[s][2], a0[s][3],
-                           a1[s][0], a1[s][1], a1[s][2], a1[s][3]};
+      for (int j = 0; j < EO_TN; ++j) {
+        const int row = j * 32 + lq;
+        bf[j] = *reinterpret_cast<const u32x4*>(bs + row * 128 +
+                                                (((2 * ks + lh) ^ ((row >> 1) & 7)) << 4));
+      }
+      const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -612,18 +646,21 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
       const u32x4 ah = u32x4{hi[0], hi[1], hi[2], hi[3]}, al = u32x4{lo[0], lo[1], lo[2], lo[3]};
 #pragma unroll
       for (int j = 0; j < EO_TN; ++j) {
-        acc[j] = mfma32x32x16<F16>(ah, bf[s][j], acc[j]);
-        acc[j] = mfma32x32x16<F16>(al, bf[s][j], acc[j]);
+        acc[j] = mfma32x32x16<F16>(ah, bf[j], acc[j]);
+        acc[j] = mfma32x32x16<F16>(al, bf[j], acc[j]);
       }
     }
-  };
-  int k = kbeg;
-  for (; k + 16 * 8 <= kbeg + kw; k += 16 * 8) batch(std::integral_constant<int, 8>{}, k);
-  if (k + 16 * 4 <= kbeg + kw) {
-    batch(std::integral_constant<int, 4>{}, k);
-    k += 16 * 4;
+    // The stage is refilled only after this wave's reads of it completed.
+    if (i + 2 < mine) {
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+      issue(wave + (i + 2) * EO_WAVES, i & 1);
+    }
   }
-  for (; k < kbeg + kw; k += 16) batch(std::integral_constant<int, 1>{}, k);
+
+  // Partial tiles of waves 1..3 through LDS (the staging area is free once
+  // every wave has passed the barrier), summed by wave 0 in wave order.
+  __syncthreads();
+  f32x16_t(*red)[EO_TN][64] = reinterpret_cast<f32x16_t(*)[EO_TN][64]>(smem);
   if (wave > 0)
 #pragma unroll
     for (int j = 0; j < EO_TN; ++j) red[wave - 1][j][lane] = acc[j];
@@ -633,11 +670,11 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
   for (int j = 0; j < EO_TN; ++j) {
 #pragma unroll
     for (int w = 0; w < EO_WAVES - 1; ++w) acc[j] += red[w][j][lane];
-    const int n = n0 + 32 * j + (lane & 31);
+    const int n = n0 + 32 * j + lq;
     const float bv = load_bias_bf16(bias, n);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int m = m0 + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (m < M) {
         const int bb = m / R, t = m - bb * R;
         const size_t yi = ((size_t)bb * T_q + t) * N + n;
@@ -739,7 +776,7 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
 hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
                             const uint16_t* bias, const OutOptions& opt, int R, int T_q,
                             hipStream_t s) {
-  if (N % (32 * EO_TN) != 0 || K % (16 * EO_WAVES) != 0) return hipErrorInvalidValue;
+  if (N % (32 * EO_TN) != 0 || K % EO_KC != 0 || M < 1) return hipErrorInvalidValue;
   dim3 grid(N / (32 * EO_TN), (M + 31) / 32);
   hipLaunchKernelGGL(early_out_kernel, grid, dim3(EO_WAVES * 64), 0, s, O32, M, K, WoT, N, bias, opt,
                      R, T_q);
