@@ -14,8 +14,14 @@ constexpr int kEarlyRows = 64;
 
 // ---- preparation ---------------------------------------------------------
 // WT[n][k] = W[k][n] for a (K x N) bf16 matrix; converted to fp16 if to_f16.
-hipError_t launch_transpose_bf16(const uint16_t* W, int K, int N, uint16_t* WT, bool to_f16,
-                                 hipStream_t s);
+struct TransposeJob {
+  const uint16_t* W;
+  uint16_t* WT;
+  int K, N;
+  int to_f16;
+};
+// j0 and, if j1 is non-null, j1 in one launch.
+hipError_t launch_transpose_bf16(const TransposeJob& j0, const TransposeJob* j1, hipStream_t s);
 // kend[b] = 1 + last index j with mask[b][j] == 0, or 0 if every key is masked.
 hipError_t launch_mask_extent(const uint8_t* mask, int B, int T_k, int* kend, hipStream_t s);
 

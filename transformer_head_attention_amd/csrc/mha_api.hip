@@ -359,9 +359,10 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     const uint16_t* bq = static_cast<const uint16_t*>(b_qkv);
 
     // prep
-    MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_qkv), D, Nqkv, wqkvT,
-                                       false, s));
-    MHA_HIP(mha::launch_transpose_bf16(static_cast<const uint16_t*>(w_o), D, D, woT, true, s));
+    // both weight transposes in one launch
+    const mha::TransposeJob tq{static_cast<const uint16_t*>(w_qkv), wqkvT, D, Nqkv, 0};
+    const mha::TransposeJob to{static_cast<const uint16_t*>(w_o), woT, D, D, 1};
+    MHA_HIP(mha::launch_transpose_bf16(tq, &to, s));
     if (key_padding_mask) {
       MHA_HIP(mha::launch_mask_extent(key_padding_mask, B, T_k, kend, s));
       MHA_HIP(mha::launch_mask_bits(key_padding_mask, B, T_k, mbits, s));

@@ -10,16 +10,24 @@ namespace {
 
 constexpr int TT = 64;   // transpose tile edge
 
-// WT[n][k] = W[k][n]; one 64 x 64 tile per workgroup, 256 threads. Global
-// traffic moves 16 bytes per lane both ways: rows of W are read as 8-element
-// chunks, and each output chunk gathers 8 consecutive k of one column from
-// LDS (rows padded by 16 bytes, so the 8 lanes gathering one column chunk
-// hit different banks). Requires K and N to be multiples of 8.
-template <bool TO_F16>
+// WT[n][k] = W[k][n] for up to two matrices in one launch (the first
+// `tiles0` workgroups take the first, the rest the second); one 64 x 64 tile
+// per workgroup, 256 threads. Global traffic moves 16 bytes per lane both
+// ways: rows of W are read as 8-element chunks, and each output chunk gathers
+// 8 consecutive k of one column from LDS (rows padded by 16 bytes, so the 8
+// lanes gathering one column chunk hit different banks). Requires K and N to
+// be multiples of 8.
 __global__ void __launch_bounds__(256)
-transpose_bf16_kernel(const uint16_t* __restrict__ W, int K, int N, uint16_t* __restrict__ WT) {
+transpose_bf16_kernel(TransposeJob j0, TransposeJob j1, int tiles0) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[TT][TT + 8];
-  const int n0 = blockIdx.x * TT, k0 = blockIdx.y * TT;
+  const bool second = (int)blockIdx.x >= tiles0;
+  const TransposeJob& jb = second ? j1 : j0;
+  const int blk = second ? (int)blockIdx.x - tiles0 : (int)blockIdx.x;
+  const uint16_t* __restrict__ W = jb.W;
+  uint16_t* __restrict__ WT = jb.WT;
+  const int K = jb.K, N = jb.N;
+  const int ntx = (N + TT - 1) / TT;
+  const int n0 = (blk % ntx) * TT, k0 = (blk / ntx) * TT;
   const int t = threadIdx.x, r = t >> 3, c = t & 7;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -37,7 +45,7 @@ transpose_bf16_kernel(const uint16_t* __restrict__ W, int K, int N, uint16_t* __
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint16_t v = tile[8 * c + j][nr];
-        if (TO_F16) v = float_to_f16_bits(bf16_bits_to_float(v));
+        if (jb.to_f16) v = float_to_f16_bits(bf16_bits_to_float(v));
         e[j] = v;
       }
       *reinterpret_cast<u32x4*>(WT + (size_t)n * K + k) =
@@ -63,13 +71,15 @@ mask_extent_kernel(const uint8_t* __restrict__ mask, int T_k, int* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_transpose_bf16(const uint16_t* W, int K, int N, uint16_t* WT, bool to_f16,
-                                 hipStream_t s) {
-  dim3 grid((N + TT - 1) / TT, (K + TT - 1) / TT);
-  if (to_f16)
-    hipLaunchKernelGGL(transpose_bf16_kernel<true>, grid, dim3(256), 0, s, W, K, N, WT);
-  else
-    hipLaunchKernelGGL(transpose_bf16_kernel<false>, grid, dim3(256), 0, s, W, K, N, WT);
+static int transpose_tiles(const TransposeJob& j) {
+  return ((j.N + TT - 1) / TT) * ((j.K + TT - 1) / TT);
+}
+
+hipError_t launch_transpose_bf16(const TransposeJob& j0, const TransposeJob* j1, hipStream_t s) {
+  const long long t0 = transpose_tiles(j0), t1 = j1 ? transpose_tiles(*j1) : 0;
+  if (t0 + t1 < 1 || t0 + t1 > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(t0 + t1)), dim3(256), 0, s, j0,
+                     j1 ? *j1 : j0, (int)t0);
   return hipGetLastError();
 }
 
