@@ -21,10 +21,12 @@ LIB = os.path.join(PKG, "libmha.so")
 SOURCES = ["mha_api.hip", "prep.hip", "gemm16.hip", "attn16.hip", "fp32_path.hip", "decode.hip",
            "weights.hip"]
 
-# Per-source extra flags. The attention kernel keeps its MFMA accumulators in
-# ordinary VGPRs (no AGPR copies around the softmax); the large GEMM tiles need
+# Per-source extra flags. The attention and decode kernels keep their MFMA
+# accumulators in ordinary VGPRs (no AGPR copies around the softmax; the d_k =
+# 128 decode kernel drops from 309 to 239 registers); the large GEMM tiles need
 # the AGPR file for their 256 accumulators per lane.
-EXTRA = {"attn16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA = {"attn16.hip": _VGPR_MFMA, "decode.hip": _VGPR_MFMA}
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
