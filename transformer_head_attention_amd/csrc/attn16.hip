@@ -246,23 +246,26 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   // Issue the DMA loads of key tile `tile` into LDS stage `stage`. Lane
   // chunk p of each wave-wide instruction lands at byte 16*p of the wave's
   // contiguous 1 KiB window; the lane fetches the global chunk that the
-  // swizzled layout places there.
+  // swizzled layout places there. Successive instructions of a tile move 32
+  // (K, d_k = 64; V) or 16 (K, d_k = 128) rows on, which leaves the swizzle
+  // unchanged, so one byte offset per lane serves all of them: each copy is
+  // a scalar base plus that offset (no per-copy address arithmetic).
+  static_assert((NT / KCH) % 16 == 0 && (NT / 8) % 16 == 0, "swizzle period");
+  const int krow0 = tid / KCH, vrow0 = tid / 8;
+  const uint32_t koff = (uint32_t)(krow0 * DK + swz<KCH>(krow0, tid % KCH) * 8) * 2u;
+  const uint32_t voff = (uint32_t)(vrow0 * a.Tkp + swz<8>(vrow0, tid % 8) * 8) * 2u;
   auto issue = [&](int tile, int stage) __attribute__((always_inline)) {
     const int k0 = tile * BLOCK_N;
     uint8_t* kst = smem + stage * STAGE;
     uint8_t* vst = kst + K_BYTES;
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(Kg + (size_t)k0 * DK);
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(Vg + k0);
 #pragma unroll
-    for (int i = 0; i < K_LPT; ++i) {
-      const int p = i * NT + tid, row = p / KCH, c = swz<KCH>(row, p % KCH);
-      lds_dma16(Kg + (size_t)(k0 + row) * DK + c * 8,
-                kst + (i * NT + wave * 64) * 16);
-    }
+    for (int i = 0; i < K_LPT; ++i)
+      lds_dma16(kb + (size_t)i * (NT / KCH) * DK * 2 + koff, kst + (i * NT + wave * 64) * 16);
 #pragma unroll
-    for (int i = 0; i < V_LPT; ++i) {
-      const int p = i * NT + tid, row = p / 8, c = swz<8>(row, p % 8);
-      lds_dma16(Vg + (size_t)row * a.Tkp + k0 + c * 8,
-                vst + (i * NT + wave * 64) * 16);
-    }
+    for (int i = 0; i < V_LPT; ++i)
+      lds_dma16(vb + (size_t)i * (NT / 8) * a.Tkp * 2 + voff, vst + (i * NT + wave * 64) * 16);
     if (HAS_MASK) {
       // The tile's two mask dwords; every wave writes the same bytes.
       if (lane < 2)
