@@ -111,6 +111,14 @@ MID = [
     ("bf16 T=65 causal", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=2, T_q=65, T_k=65)),
     ("bf16 T=129 causal d_k=128", W["causal_bf16_d4096_h32_b1_t8192"], dict(D=1024, h=8,
                                                                               T_q=129, T_k=129)),
+    # small d_model: the early-row projection's 64-deep K chunks are dealt
+    # unevenly to its four waves (D=128: two chunks, D=384: 2/2/1/1)
+    ("bf16 causal D=128 h=2", W["causal_bf16_d512_h8_b16_t1024"], dict(D=128, h=2, B=2, T_q=150,
+                                                                       T_k=150)),
+    ("bf16 causal D=128 h=1 d_k=128", W["causal_bf16_d4096_h32_b1_t8192"],
+     dict(D=128, h=1, B=2, T_q=70, T_k=70)),
+    ("bf16 causal D=384 h=6 ragged", W["causal_bf16_d512_h8_b16_t1024"],
+     dict(D=384, h=6, B=2, T_q=211, T_k=211)),
     # grouped key/value heads
     ("bf16 GQA g4 causal d1024 ragged", W["causal_bf16_d1024_h16_b8_t4096"],
      dict(B=1, T_q=777, T_k=777, n_kv=4)),
