@@ -218,17 +218,43 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, lh = lane >> 5;
 
-  // Workgroup -> (batch, head, query block). All query blocks of one
-  // (batch, head) run on one XCD and share its L2 copy of K and V; under the
-  // causal mask the longest blocks are dispatched first.
+  // Workgroup -> (batch, head, query block). All query blocks of the heads
+  // that share one key/value set run on one XCD and share its L2 copy of K
+  // and V; under the causal mask the longest blocks are dispatched first.
+  // With a padding mask the work of a batch element grows with its key
+  // extent: the units (batch element, key/value set) are taken in `order`
+  // (longest extent first) and dealt round-robin to the 8 XCDs (hardware
+  // block L runs on XCD L % 8), so every XCD gets a like share and starts
+  // with its longest units.
   const int nqb = a.Tqp / BLOCK_M;
-  const int logical = xcd_remap((int)blockIdx.x - early_slots, nqb * a.h * a.B);
-  const int bh = logical / nqb;
-  int qblk = logical - bh * nqb;
+  const int L = (int)blockIdx.x - early_slots;
+  int b, head, qblk;
+  if (HAS_MASK && a.order != nullptr) {
+    const int gh = a.h / a.h_kv, WU = gh * nqb, U = a.B * a.h_kv;
+    int us, w;
+    if (U % 8 == 0) {
+      const int idx = L >> 3, j = idx / WU;
+      us = (L & 7) + 8 * j;
+      w = idx - j * WU;
+    } else {
+      us = L / WU;
+      w = L - us * WU;
+    }
+    const int r = us / a.h_kv;
+    b = a.order[r];
+    head = (us - r * a.h_kv) * gh + w / nqb;
+    qblk = w % nqb;
+  } else {
+    const int logical = xcd_remap(L, nqb * a.h * a.B);
+    const int bh0 = logical / nqb;
+    qblk = logical - bh0 * nqb;
+    b = bh0 / a.h;
+    head = bh0 - b * a.h;
+  }
   if (a.causal) qblk = nqb - 1 - qblk;
-  const int b = bh / a.h, head = bh - b * a.h;
+  const int bh = b * a.h + head;
   // Key/value set of this query head: consecutive heads share one set, and
-  // their workgroups are consecutive in the XCD mapping above, so a set's K
+  // their workgroups are consecutive in the XCD mappings above, so a set's K
   // and V are read into one XCD's L2 for the whole group.
   const int kvh = b * a.h_kv + head / (a.h / a.h_kv);
 

@@ -24,6 +24,9 @@ struct TransposeJob {
 hipError_t launch_transpose_bf16(const TransposeJob& j0, const TransposeJob* j1, hipStream_t s);
 // kend[b] = 1 + last index j with mask[b][j] == 0, or 0 if every key is masked.
 hipError_t launch_mask_extent(const uint8_t* mask, int B, int T_k, int* kend, hipStream_t s);
+// order[r] = the batch element with the r-th largest kend (ties by index).
+constexpr int kMaskOrderMaxB = 1024;
+hipError_t launch_mask_order(const int* kend, int B, int* order, hipStream_t s);
 
 // ---- 16-bit MFMA GEMMs (C = A . Bt^T, both operands K-contiguous) -------
 // Columns of [Q | K | V]: Q is D wide (h heads), K and V are Dkv = h_kv * d_k
@@ -72,6 +75,8 @@ struct AttnF16Args {
   const uint32_t* mbits;  // (B, mbits_ld, 2) ignore bitmask per 64-key tile, or null
   int mbits_ld;           // 64-key tiles per batch element (attn_mask_tiles(T_k))
   const int* kend;     // (B) key extent from the mask; read only with mbits
+  const int* order;    // (B) batch elements by key extent, longest first; read only
+                       // with mbits; null: natural order
   int B, h, h_kv, T_q, T_k, Tqp, Tkp, D, causal;
 };
 int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp, Tkp must be multiples)

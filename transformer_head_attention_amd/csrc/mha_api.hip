@@ -53,7 +53,7 @@ int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
 struct Layout {
   // byte offsets into the workspace
-  size_t wqkvT = 0, woT = 0, q = 0, k = 0, vt = 0, o = 0, kend = 0, mbits = 0, eqkv = 0,
+  size_t wqkvT = 0, woT = 0, q = 0, k = 0, vt = 0, o = 0, kend = 0, order = 0, mbits = 0, eqkv = 0,
          eo = 0;
   size_t f_q = 0, f_kv = 0, f_o = 0;
   size_t total = 0;
@@ -82,6 +82,7 @@ Layout make_layout(const mha_handle* hd, int B, int T_q, int T_k) {
     L.vt = take((size_t)B * L.Tkp * Dkv * 2);
     L.o = take((size_t)B * T_q * D * 2);
     L.kend = take((size_t)B * 4);
+    L.order = take((size_t)B * 4);
     L.mbits = take((size_t)B * mha::attn_mask_tiles(T_k) * 8);
     L.eqkv = take((size_t)B * L.R * Nqkv * 4);
     L.eo = take((size_t)B * L.R * D * 4);
@@ -354,6 +355,10 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     uint16_t* o = reinterpret_cast<uint16_t*>(ws + L.o);
     int* kend = reinterpret_cast<int*>(ws + L.kend);
     uint32_t* mbits = reinterpret_cast<uint32_t*>(ws + L.mbits);
+    int* order = reinterpret_cast<int*>(ws + L.order);
+    // padding masks: batch elements by key extent for the attention launch's
+    // longest-first order (natural order past kMaskOrderMaxB)
+    const bool ordered = key_padding_mask && B <= mha::kMaskOrderMaxB;
     float* eqkv = reinterpret_cast<float*>(ws + L.eqkv);
     float* eo = reinterpret_cast<float*>(ws + L.eo);
     const uint16_t* bq = static_cast<const uint16_t*>(b_qkv);
@@ -365,6 +370,7 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     MHA_HIP(mha::launch_transpose_bf16(tq, &to, s));
     if (key_padding_mask) {
       MHA_HIP(mha::launch_mask_extent(key_padding_mask, B, T_k, kend, s));
+      if (ordered) MHA_HIP(mha::launch_mask_order(kend, B, order, s));
       MHA_HIP(mha::launch_mask_bits(key_padding_mask, B, T_k, mbits, s));
     }
     if (!mark(1)) return MHA_ERR_HIP;
@@ -410,6 +416,7 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     a.mbits = key_padding_mask ? mbits : nullptr;
     a.mbits_ld = mha::attn_mask_tiles(T_k);
     a.kend = key_padding_mask ? kend : nullptr;
+    a.order = ordered ? order : nullptr;
     a.B = B;
     a.h = h;
     a.h_kv = h_kv;

@@ -69,6 +69,21 @@ mask_extent_kernel(const uint8_t* __restrict__ mask, int T_k, int* __restrict__ 
   if (threadIdx.x == 0) kend[b] = max(max(red[0], red[1]), max(red[2], red[3])) + 1;
 }
 
+// Rank of each batch element by key extent (descending, ties by index); every
+// workgroup stages all B extents in LDS and ranks 256 of them. B <= 1024.
+__global__ void __launch_bounds__(256)
+mask_order_kernel(const int* __restrict__ kend, int B, int* __restrict__ order) {
+  __shared__ int ke[kMaskOrderMaxB];
+  for (int i = threadIdx.x; i < B; i += 256) ke[i] = kend[i];
+  __syncthreads();
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int mine = ke[b];
+  int rank = 0;
+  for (int i = 0; i < B; ++i) rank += (ke[i] > mine || (ke[i] == mine && i < b)) ? 1 : 0;
+  order[rank] = b;
+}
+
 }  // namespace
 
 static int transpose_tiles(const TransposeJob& j) {
@@ -80,6 +95,12 @@ hipError_t launch_transpose_bf16(const TransposeJob& j0, const TransposeJob* j1,
   if (t0 + t1 < 1 || t0 + t1 > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(t0 + t1)), dim3(256), 0, s, j0,
                      j1 ? *j1 : j0, (int)t0);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_order(const int* kend, int B, int* order, hipStream_t s) {
+  if (B < 1 || B > kMaskOrderMaxB) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mask_order_kernel, dim3((B + 255) / 256), dim3(256), 0, s, kend, B, order);
   return hipGetLastError();
 }
 
