@@ -246,8 +246,21 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
     qblk = w % nqb;
   } else {
     const int logical = xcd_remap(L, nqb * a.h * a.B);
-    const int bh0 = logical / nqb;
-    qblk = logical - bh0 * nqb;
+    int bh0;
+    if (a.group_units > 1 && a.causal) {
+      // Groups of G (batch, head) units: their query blocks interleaved
+      // longest first, so the long blocks of the last units of an XCD do not
+      // trail at the end of the launch (G is bounded by the L2 footprint of
+      // the group's K and V).
+      const int G = a.group_units, units = a.h * a.B;
+      const int g0 = (logical / (G * nqb)) * G, gs = min(G, units - g0);
+      const int pos = logical - g0 * nqb;
+      bh0 = g0 + pos % gs;
+      qblk = pos / gs;
+    } else {
+      bh0 = logical / nqb;
+      qblk = logical - bh0 * nqb;
+    }
     b = bh0 / a.h;
     head = bh0 - b * a.h;
   }
@@ -585,9 +598,22 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
   }
   const int bm = attn_f16_block_m(d_k);
   const int total = (a.Tqp / bm) * a.h * a.B;
+  // Causal, unpadded: query blocks of groups of G units are interleaved
+  // longest first. G keeps the group's K and V (4 Tkp d_k bytes per key/value
+  // set, shared by h / h_kv heads) within about 8 MiB of an XCD's L2 and
+  // Infinity Cache share, at most 16 and at most the units one XCD runs.
+  AttnF16Args ag = a;
+  ag.group_units = 1;
+  if (a.causal && !a.mbits) {
+    const long long unit_kv = 4LL * a.Tkp * d_k / (a.h / a.h_kv);
+    const long long per_xcd = (long long)a.h * a.B / 8;
+    while (ag.group_units < 16 && 2LL * ag.group_units * unit_kv <= (8LL << 20) &&
+           2LL * ag.group_units <= per_xcd)
+      ag.group_units *= 2;
+  }
   if ((long long)total + extra > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (d_k == 64) return launch_dk<64, MHA_ATTN_NS64>(a, total, e, extra, s);
-  if (d_k == 128) return launch_dk<128, MHA_ATTN_NS128>(a, total, e, extra, s);
+  if (d_k == 64) return launch_dk<64, MHA_ATTN_NS64>(ag, total, e, extra, s);
+  if (d_k == 128) return launch_dk<128, MHA_ATTN_NS128>(ag, total, e, extra, s);
   return hipErrorInvalidValue;
 }
 

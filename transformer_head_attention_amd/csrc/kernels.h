@@ -78,6 +78,7 @@ struct AttnF16Args {
   const int* order;    // (B) batch elements by key extent, longest first; read only
                        // with mbits; null: natural order
   int B, h, h_kv, T_q, T_k, Tqp, Tkp, D, causal;
+  int group_units;     // set by launch_attn_f16 (causal query-block interleave)
 };
 int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp, Tkp must be multiples)
 int attn_mask_tiles(int T_k);    // 64-key tiles covering T_k
