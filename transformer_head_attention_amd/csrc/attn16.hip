@@ -47,6 +47,10 @@ namespace mha {
 
 namespace {
 
+// K and V bytes a group of interleaved causal units may span: one XCD's L2.
+#ifndef MHA_ATTN_GROUP_BYTES
+#define MHA_ATTN_GROUP_BYTES (4LL << 20)
+#endif
 constexpr int BLOCK_N = 64;   // keys per tile
 constexpr int NWAVES = 4;
 constexpr int NT = NWAVES * 64;
@@ -600,14 +604,14 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
   const int total = (a.Tqp / bm) * a.h * a.B;
   // Causal, unpadded: query blocks of groups of G units are interleaved
   // longest first. G keeps the group's K and V (4 Tkp d_k bytes per key/value
-  // set, shared by h / h_kv heads) within about 8 MiB of an XCD's L2 and
-  // Infinity Cache share, at most 16 and at most the units one XCD runs.
+  // set, shared by h / h_kv heads) within one XCD's L2, at most 16 and at
+  // most the units one XCD runs.
   AttnF16Args ag = a;
   ag.group_units = 1;
   if (a.causal && !a.mbits) {
     const long long unit_kv = 4LL * a.Tkp * d_k / (a.h / a.h_kv);
     const long long per_xcd = (long long)a.h * a.B / 8;
-    while (ag.group_units < 16 && 2LL * ag.group_units * unit_kv <= (8LL << 20) &&
+    while (ag.group_units < 16 && 2LL * ag.group_units * unit_kv <= MHA_ATTN_GROUP_BYTES &&
            2LL * ag.group_units <= per_xcd)
       ag.group_units *= 2;
   }
