@@ -482,9 +482,14 @@ struct VEpi {
   }
 };
 
-// fp32 result epilogue of the output projection, on transposed tiles: a lane
-// holds row m and four consecutive columns n..n+3 per fragment group, which
-// go out as one 16-byte store (four stores cover a 128-byte line of a row).
+// Result epilogue of the output projection, on transposed tiles: a lane holds
+// row m and four consecutive columns n..n+3 per fragment group. The bias is
+// added in registers; each 32-row block of the wave's tile then goes through
+// the wave's LDS window (fp32, 16-byte chunks XOR-swizzled by row so that
+// both the fragment writes and the row reads are free of bank conflicts) and
+// out row by row: one store instruction covers two whole row segments of the
+// tile (WN * 4 bytes each), the residual (bf16) is read in the same order and
+// the bf16 result, if asked for, converted there.
 template <bool RESID, bool YBF16>
 struct OutEpi {
   const uint16_t* bias;
@@ -492,7 +497,9 @@ struct OutEpi {
   const uint16_t* resid; // (M x N) bf16 added to the result with RESID
   template <int TM, int TN>
   __device__ __forceinline__ void apply(f32x16_t (&acc)[TM][TN], int mbase, int nbase, int lane,
-                                        int M, int N, uint8_t* /*lds*/) const {
+                                        int M, int N, uint8_t* lds) const {
+    constexpr int WN = TN * 32, CPR = WN / 4;   // 16-byte chunks per staged row
+    static_assert(CPR == 16 || CPR == 32, "staged row width");
     const int lq = lane & 31, lh = lane >> 5;
     // The wave's bias values, fetched together (clamped to the last columns;
     // values past N are never stored).
@@ -509,46 +516,56 @@ struct OutEpi {
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) bb[j][rg] = u32x2{0u, 0u};
     }
-    const bool full = mbase + TM * 32 <= M && nbase + TN * 32 <= N;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int m = mbase + i * 32 + lq;
-      // The row's residual values, fetched together (rows past M read row M-1).
-      u32x2 rr[TN][4];
-      if constexpr (RESID) {
-        const uint16_t* xr = resid + (size_t)min(m, M - 1) * N;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg)
-            rr[j][rg] = *reinterpret_cast<const u32x2*>(xr + min(nbase + j * 32 + 8 * rg + 4 * lh, N - 4));
-      }
+      // fragments of rows i*32 .. i*32+31 into LDS (row lq, chunk 8 j + 2 rg + lh)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const int c = j * 32 + 8 * rg + 4 * lh;
           const f32x16_t& a = acc[i][j];
           const u32x2 b2 = bb[j][rg];
-          f32x4_t v = {a[rg * 4 + 0] + __uint_as_float(b2.x << 16),
-                       a[rg * 4 + 1] + __uint_as_float(b2.x & 0xffff0000u),
-                       a[rg * 4 + 2] + __uint_as_float(b2.y << 16),
-                       a[rg * 4 + 3] + __uint_as_float(b2.y & 0xffff0000u)};
-          if constexpr (RESID) {
-            const u32x2 r2 = rr[j][rg];
-            v[0] += __uint_as_float(r2.x << 16);
-            v[1] += __uint_as_float(r2.x & 0xffff0000u);
-            v[2] += __uint_as_float(r2.y << 16);
-            v[3] += __uint_as_float(r2.y & 0xffff0000u);
-          }
-          if (full || (m < M && nbase + c < N)) {
-            if constexpr (YBF16)
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Y) + (size_t)m * N + nbase + c) =
-                  u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            else
-              *reinterpret_cast<f32x4_t*>(static_cast<float*>(Y) + (size_t)m * N + nbase + c) = v;
-          }
+          const f32x4_t v = {a[rg * 4 + 0] + __uint_as_float(b2.x << 16),
+                             a[rg * 4 + 1] + __uint_as_float(b2.x & 0xffff0000u),
+                             a[rg * 4 + 2] + __uint_as_float(b2.y << 16),
+                             a[rg * 4 + 3] + __uint_as_float(b2.y & 0xffff0000u)};
+          const int c = 8 * j + 2 * rg + lh;
+          *reinterpret_cast<f32x4_t*>(lds + lq * (CPR * 16) + ((c ^ (lq & 15)) << 4)) = v;
         }
+      // rows out: 64 / CPR rows per instruction, each row segment contiguous;
+      // the block's residual values are fetched together first (one latency)
+      constexpr int KO = 32 * CPR / 64;
+      u32x2 rr[RESID ? KO : 1];
+      if constexpr (RESID) {
+#pragma unroll
+        for (int k = 0; k < KO; ++k) {
+          const int idx = k * 64 + lane, r = idx / CPR, c = idx % CPR;
+          const int m = min(mbase + i * 32 + r, M - 1), n = min(nbase + 4 * c, N - 4);
+          rr[k] = *reinterpret_cast<const u32x2*>(resid + (size_t)m * N + n);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+#pragma unroll
+      for (int k = 0; k < KO; ++k) {
+        const int idx = k * 64 + lane, r = idx / CPR, c = idx % CPR;
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(lds + r * (CPR * 16) + ((c ^ (r & 15)) << 4));
+        const int m = mbase + i * 32 + r, n = nbase + 4 * c;
+        if (m >= M || n >= N) continue;
+        const size_t yi = (size_t)m * N + n;
+        if constexpr (RESID) {
+          const u32x2 r2 = rr[k];
+          v[0] += __uint_as_float(r2.x << 16);
+          v[1] += __uint_as_float(r2.x & 0xffff0000u);
+          v[2] += __uint_as_float(r2.y << 16);
+          v[3] += __uint_as_float(r2.y & 0xffff0000u);
+        }
+        if constexpr (YBF16)
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Y) + yi) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        else
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(Y) + yi) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // reads done before the next block
       __builtin_amdgcn_sched_barrier(0);
     }
   }
