@@ -104,6 +104,9 @@ MID = [
     ("bf16 causal d_k=128", W["causal_bf16_d4096_h32_b1_t8192"], dict(T_q=300, T_k=300)),
     ("bf16 causal + padding", W["causal_bf16_d512_h8_b16_t1024"],
      dict(B=3, T_q=190, T_k=190, padding=(150, 190))),
+    # more batch elements than the extent ranking takes: natural order
+    ("bf16 cross padded B=1100", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
+     dict(B=1100, T_q=5, T_k=12, padding=(1, 12))),
     ("bf16 T=1 causal", W["causal_bf16_d512_h8_b16_t1024"], dict(B=3, T_q=1, T_k=1)),
     ("bf16 T=1 self", W["causal_bf16_d512_h8_b16_t1024"], dict(B=3, T_q=1, T_k=1, causal=False)),
     ("bf16 T_q=1 cross", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
