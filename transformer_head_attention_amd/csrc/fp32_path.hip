@@ -2,13 +2,16 @@
 //
 //  * gemm_f32: C = A . B + bias with v_mfma_f32_16x16x4_f32 (full fp32
 //    products and sums); B and bias may be stored as bf16 (converted exactly).
+//    64-deep K slices, the next one loaded into registers under the current
+//    one's MFMAs.
 //    Used for X . W_QKV and O . W_O (itwiki "멀티 헤드 어텐션",
 //    텐서 모양으로 본 계산, 투영 and 출력 투영 rows).
 //  * attn_f32: softmax(q . k / sqrt(d_k) + M) v row by row in fp32
 //    (same page, 수식; iamjaehka13.blog "[Deep Learning 5]", §7-§13). Each
 //    query row is shared by d_k/16 lanes that each own 16 of its dimensions;
-//    keys are staged through LDS in chunks of 64 and folded into a running
-//    max / running sum.
+//    keys are staged through LDS in chunks of 64, split over the four waves
+//    of a workgroup, folded into running max / sum states that are merged at
+//    the end.
 #include <math.h>
 
 #include "device_common.h"
@@ -18,8 +21,11 @@ namespace mha {
 
 namespace {
 
-constexpr int FBM = 64, FBN = 64, FBK = 16;
+constexpr int FBM = 64, FBN = 64, FBK = 64;
 
+// 64 x 64 tile per workgroup (4 waves of 32 x 32), K in 64-deep slices; the
+// next slice is loaded into registers while the current one is multiplied
+// from LDS, so each slice costs one global latency at most once.
 template <bool B_BF16>
 __global__ void __launch_bounds__(256)
 gemm_f32_kernel(const float* __restrict__ A, int lda, int M, int K, const void* __restrict__ Bv,
@@ -37,30 +43,65 @@ gemm_f32_kernel(const float* __restrict__ A, int lda, int M, int K, const void* 
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < K; k0 += FBK) {
-    {
-      const int row = tid >> 2, c = (tid & 3) * 4;
-      const int m = min(m0 + row, M - 1);
-      const float4 v = *reinterpret_cast<const float4*>(A + (size_t)m * lda + k0 + c);
-      As[row][c] = v.x; As[row][c + 1] = v.y; As[row][c + 2] = v.z; As[row][c + 3] = v.w;
+  // A slice: 64 rows x 64 k (4 float4 per thread); B slice: 64 k x 64 n, as
+  // 4 float4 (fp32) or 2 x 8 bf16 per thread. Rows past M are clamped (never
+  // stored); N is a multiple of 64 here.
+  f32x4_t ra[4], rb[4];
+  u32x4 rbh[2];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = i * 256 + tid, row = p >> 4, c = (p & 15) * 4;
+      ra[i] = *reinterpret_cast<const f32x4_t*>(A + (size_t)min(m0 + row, M - 1) * lda + k0 + c);
     }
     if (!B_BF16) {
       const float* Bf = static_cast<const float*>(Bv);
-      const int row = tid >> 4, c = (tid & 15) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(Bf + (size_t)(k0 + row) * ldb + n0 + c);
-      Bs[row][c] = v.x; Bs[row][c + 1] = v.y; Bs[row][c + 2] = v.z; Bs[row][c + 3] = v.w;
-    } else if (tid < 128) {
-      const uint16_t* Bb = static_cast<const uint16_t*>(Bv);
-      const int row = tid >> 3, c = (tid & 7) * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(Bb + (size_t)(k0 + row) * ldb + n0 + c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Bs[row][c + 2 * e] = __uint_as_float(w[e] << 16);
-        Bs[row][c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      for (int i = 0; i < 4; ++i) {
+        const int p = i * 256 + tid, row = p >> 4, c = (p & 15) * 4;
+        rb[i] = *reinterpret_cast<const f32x4_t*>(Bf + (size_t)(k0 + row) * ldb + n0 + c);
+      }
+    } else {
+      const uint16_t* Bb = static_cast<const uint16_t*>(Bv);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int p = i * 256 + tid, row = p >> 3, c = (p & 7) * 8;
+        rbh[i] = *reinterpret_cast<const u32x4*>(Bb + (size_t)(k0 + row) * ldb + n0 + c);
       }
     }
+  };
+  auto stash = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = i * 256 + tid, row = p >> 4, c = (p & 15) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[row][c + e] = ra[i][e];
+    }
+    if (!B_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = i * 256 + tid, row = p >> 4, c = (p & 15) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[row][c + e] = rb[i][e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int p = i * 256 + tid, row = p >> 3, c = (p & 7) * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Bs[row][c + 2 * e] = __uint_as_float(rbh[i][e] << 16);
+          Bs[row][c + 2 * e + 1] = __uint_as_float(rbh[i][e] & 0xffff0000u);
+        }
+      }
+    }
+  };
+
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += FBK) {
+    stash();
     __syncthreads();
+    if (k0 + FBK < K) load(k0 + FBK);
 #pragma unroll
     for (int kk = 0; kk < FBK / 4; ++kk) {
       float av[2], bv[2];
@@ -100,27 +141,37 @@ gemm_f32_kernel(const float* __restrict__ A, int lda, int M, int K, const void* 
 }
 
 constexpr int KC = 64;           // keys per LDS chunk
-constexpr int ATTN32_NT = 256;   // threads per workgroup
+constexpr int ATTN32_NT = 256;   // threads per workgroup (4 waves)
+constexpr int KW = KC / 4;       // keys of a chunk per wave
 
+// A workgroup takes 64 / (d_k/16) query rows (16 at d_k = 64, 8 at 128);
+// each wave holds all of them and takes a quarter of every 64-key chunk
+// (keys 16 w .. 16 w + 15), with its own running max, sum and accumulator;
+// the four partial states are merged through LDS at the end. Scores in log2
+// units (q . k times log2(e)/sqrt(d_k)), exponentials exp2.
 template <int DK>
 __global__ void __launch_bounds__(ATTN32_NT)
 attn_f32_kernel(AttnF32Args a) {
-  constexpr int TPR = DK / 16;           // lanes per query row
-  constexpr int RPB = ATTN32_NT / TPR;   // query rows per workgroup
+  constexpr int TPR = DK / 16;    // lanes per query row
+  constexpr int RPB = 64 / TPR;   // query rows per workgroup
   __shared__ __attribute__((aligned(16))) float Ks[KC][DK];
   __shared__ __attribute__((aligned(16))) float Vs[KC][DK];
+  __shared__ uint8_t Ms[KC];
+  __shared__ float m_s[4][RPB], l_s[4][RPB];
 
-  const int tid = threadIdx.x, r = tid / TPR, p = tid % TPR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane / TPR, p = lane % TPR;
   const int head = blockIdx.y, b = blockIdx.z;
   const int t = blockIdx.x * RPB + r;
   const bool valid = t < a.rows;
-  const float scale = 1.0f / sqrtf((float)DK);
+  const float scale = 1.4426950408889634f / sqrtf((float)DK);
 
   float q[16], acc[16];
-  const float* qp = a.q + (size_t)b * a.q_bstride + (size_t)t * a.q_ld + head * DK + p * 16;
+  const float* qp = a.q + (size_t)b * a.q_bstride + (size_t)(valid ? t : 0) * a.q_ld + head * DK +
+                    p * 16;
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
-    q[c] = valid ? qp[c] : 0.0f;
+    q[c] = valid ? qp[c] * scale : 0.0f;
     acc[c] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
@@ -143,43 +194,69 @@ attn_f32_kernel(AttnF32Args a) {
       *reinterpret_cast<float4*>(&Ks[key][c4]) = kv;
       *reinterpret_cast<float4*>(&Vs[key][c4]) = vv;
     }
+    if (tid < KC) Ms[tid] = (mb && j0 + tid < a.T_k) ? mb[j0 + tid] : 0;
     __syncthreads();
 
-    float s[KC];
+    float s[KW];
     float cmax = -INFINITY;
 #pragma unroll
-    for (int jj = 0; jj < KC; ++jj) {
+    for (int jj = 0; jj < KW; ++jj) {
+      const int kk = wave * KW + jj, j = j0 + kk;
       float part = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) part = __builtin_fmaf(q[c], Ks[jj][p * 16 + c], part);
+      for (int c = 0; c < 16; ++c) part = __builtin_fmaf(q[c], Ks[kk][p * 16 + c], part);
 #pragma unroll
       for (int off = 1; off < TPR; off <<= 1) part += __shfl_xor(part, off);
-      const int j = j0 + jj;
-      const bool ign = j >= a.T_k || (a.causal && j > t) || (mb && mb[j] != 0);
-      s[jj] = ign ? -INFINITY : part * scale;
+      const bool ign = j >= a.T_k || (a.causal && j > t) || Ms[kk] != 0;
+      s[jj] = ign ? -INFINITY : part;
       cmax = fmaxf(cmax, s[jj]);
     }
     const float m_new = fmaxf(m, cmax);
     const float base = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = expf(m - base);
+    const float corr = exp2f(m - base);
     l *= corr;
 #pragma unroll
     for (int c = 0; c < 16; ++c) acc[c] *= corr;
 #pragma unroll
-    for (int jj = 0; jj < KC; ++jj) {
-      const float pj = expf(s[jj] - base);
+    for (int jj = 0; jj < KW; ++jj) {
+      const float pj = exp2f(s[jj] - base);
       l += pj;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) acc[c] = __builtin_fmaf(pj, Vs[jj][p * 16 + c], acc[c]);
+      for (int c = 0; c < 16; ++c) acc[c] = __builtin_fmaf(pj, Vs[wave * KW + jj][p * 16 + c], acc[c]);
     }
     m = m_new;
   }
 
-  if (valid) {
-    float* op = a.o + (size_t)b * a.o_bstride + (size_t)t * a.o_ld + head * DK + p * 16;
+  // Merge the four waves' states (wave order, fixed): Ks holds the
+  // accumulators once every wave is past the last chunk.
+  __syncthreads();
+  float (*accs)[RPB][DK] = reinterpret_cast<float (*)[RPB][DK]>(&Ks[0][0]);
+  static_assert(4 * RPB * DK <= KC * DK, "merge buffer");
 #pragma unroll
-    for (int c = 0; c < 16; ++c) op[c] = acc[c] / l;
+  for (int c = 0; c < 16; ++c) accs[wave][r][p * 16 + c] = acc[c];
+  if (p == 0) {
+    m_s[wave][r] = m;
+    l_s[wave][r] = l;
   }
+  __syncthreads();
+  if (wave != 0 || !valid) return;
+  float mx = m_s[0][r];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) mx = fmaxf(mx, m_s[w][r]);
+  const float base = mx == -INFINITY ? 0.0f : mx;
+  float lt = 0.0f, o[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float f = exp2f(m_s[w][r] - base);   // 0 for a wave that saw no key
+    lt += l_s[w][r] * f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] = __builtin_fmaf(accs[w][r][p * 16 + c], f, o[c]);
+  }
+  float* op = a.o + (size_t)b * a.o_bstride + (size_t)t * a.o_ld + head * DK + p * 16;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) op[c] = o[c] / lt;   // all keys masked: 0 / 0 = NaN
 }
 
 }  // namespace
@@ -187,6 +264,7 @@ attn_f32_kernel(AttnF32Args a) {
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B, int ldb, int N,
                            bool b_bf16, const void* bias, float* C, int ldc, int rows_in,
                            int rows_out, hipStream_t s) {
+  if (K % FBK != 0 || N % FBN != 0 || M < 1) return hipErrorInvalidValue;
   dim3 grid((N + FBN - 1) / FBN, (M + FBM - 1) / FBM);
   if (b_bf16)
     hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, dim3(256), 0, s, A, lda, M, K, B, ldb, N, bias,
@@ -200,10 +278,12 @@ hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B,
 hipError_t launch_attn_f32(const AttnF32Args& a, int d_k, hipStream_t s) {
   if (a.group < 1 || a.h % a.group != 0) return hipErrorInvalidValue;
   if (d_k == 64) {
-    dim3 grid((a.rows + 63) / 64, a.h, a.B);
+    constexpr int rpb = 64 / 4;
+    dim3 grid((a.rows + rpb - 1) / rpb, a.h, a.B);
     hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(ATTN32_NT), 0, s, a);
   } else if (d_k == 128) {
-    dim3 grid((a.rows + 31) / 32, a.h, a.B);
+    constexpr int rpb = 64 / 8;
+    dim3 grid((a.rows + rpb - 1) / rpb, a.h, a.B);
     hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(ATTN32_NT), 0, s, a);
   } else {
     return hipErrorInvalidValue;
