@@ -420,6 +420,9 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
           s[qi][kh] = mfma32x32x16<F16>(kf[kh][ks], qreg[qi][ks], s[qi][kh]);
       }
     }
+    // (The V^T reads stay behind the score MFMAs: they are part of the
+    // distance between those MFMAs and the row maximum below.)
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 vf[DT][4];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
