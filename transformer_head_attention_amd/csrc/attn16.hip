@@ -557,36 +557,11 @@ hipError_t launch_dk(const AttnF16Args& a, int total, const AttnF32Args& e, int 
   return hipGetLastError();
 }
 
-// Per 64-key tile of each batch element, a 64-bit mask of the keys to
-// ignore: padding-mask nonzero, or index >= T_k. One thread per tile.
-__global__ void __launch_bounds__(256)
-mask_bits_kernel(const uint8_t* __restrict__ mask, int B, int T_k, int ntk,
-                 uint32_t* __restrict__ bits) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= B * ntk) return;
-  const int b = i / ntk, tile = i - b * ntk;
-  uint32_t w[2] = {0u, 0u};
-  for (int j = 0; j < BLOCK_N; ++j) {
-    const int key = tile * BLOCK_N + j;
-    const bool ign = key >= T_k || mask[(size_t)b * T_k + key] != 0;
-    if (ign) w[j >> 5] |= 1u << (j & 31);
-  }
-  bits[(size_t)i * 2] = w[0];
-  bits[(size_t)i * 2 + 1] = w[1];
-}
-
 }  // namespace
 
 int attn_f16_block_m(int d_k) { return NWAVES * 32 * nq_for(d_k); }
 
 int attn_mask_tiles(int T_k) { return (T_k + BLOCK_N - 1) / BLOCK_N; }
-
-hipError_t launch_mask_bits(const uint8_t* mask, int B, int T_k, uint32_t* bits, hipStream_t s) {
-  const int ntk = attn_mask_tiles(T_k);
-  hipLaunchKernelGGL(mask_bits_kernel, dim3((B * ntk + 255) / 256), dim3(256), 0, s, mask, B, T_k,
-                     ntk, bits);
-  return hipGetLastError();
-}
 
 hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* early,
                            hipStream_t s) {

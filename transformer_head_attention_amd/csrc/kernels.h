@@ -20,10 +20,18 @@ struct TransposeJob {
   int K, N;
   int to_f16;
 };
-// j0 and, if j1 is non-null, j1 in one launch.
-hipError_t launch_transpose_bf16(const TransposeJob& j0, const TransposeJob* j1, hipStream_t s);
-// kend[b] = 1 + last index j with mask[b][j] == 0, or 0 if every key is masked.
-hipError_t launch_mask_extent(const uint8_t* mask, int B, int T_k, int* kend, hipStream_t s);
+// Scan of a (B, T_k) padding mask (nonzero = ignore): kend[b] = 1 + last index
+// j with mask[b][j] == 0, or 0 if every key is masked; bits[b][tile] (two
+// uint32): bit j set if key tile*64+j is masked or >= T_k.
+struct MaskScan {
+  const uint8_t* mask;   // null: no scan
+  int B, T_k;
+  int* kend;
+  uint32_t* bits;
+};
+// The transposes j0 and (if non-null) j1 and the mask scan, in one launch.
+hipError_t launch_prep(const TransposeJob& j0, const TransposeJob* j1, const MaskScan& ms,
+                       hipStream_t s);
 // order[r] = the batch element with the r-th largest kend (ties by index).
 constexpr int kMaskOrderMaxB = 1024;
 hipError_t launch_mask_order(const int* kend, int B, int* order, hipStream_t s);
@@ -82,8 +90,6 @@ struct AttnF16Args {
 };
 int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp, Tkp must be multiples)
 int attn_mask_tiles(int T_k);    // 64-key tiles covering T_k
-// bits[b][tile] (two uint32): bit j set if key tile*64+j is masked or >= T_k.
-hipError_t launch_mask_bits(const uint8_t* mask, int B, int T_k, uint32_t* bits, hipStream_t s);
 // early (nullable): the fp32 early causal rows (rows <= T_k <= 64), evaluated
 // by extra workgroups at the start of the same launch.
 struct AttnF32Args;

@@ -364,15 +364,12 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     const uint16_t* bq = static_cast<const uint16_t*>(b_qkv);
 
     // prep
-    // both weight transposes in one launch
+    // both weight transposes and the mask scan in one launch
     const mha::TransposeJob tq{static_cast<const uint16_t*>(w_qkv), wqkvT, D, Nqkv, 0};
     const mha::TransposeJob to{static_cast<const uint16_t*>(w_o), woT, D, D, 1};
-    MHA_HIP(mha::launch_transpose_bf16(tq, &to, s));
-    if (key_padding_mask) {
-      MHA_HIP(mha::launch_mask_extent(key_padding_mask, B, T_k, kend, s));
-      if (ordered) MHA_HIP(mha::launch_mask_order(kend, B, order, s));
-      MHA_HIP(mha::launch_mask_bits(key_padding_mask, B, T_k, mbits, s));
-    }
+    const mha::MaskScan ms{key_padding_mask, B, T_k, kend, mbits};
+    MHA_HIP(mha::launch_prep(tq, &to, ms, s));
+    if (ordered) MHA_HIP(mha::launch_mask_order(kend, B, order, s));
     if (!mark(1)) return MHA_ERR_HIP;
 
     // qkv_proj

@@ -1,6 +1,7 @@
 // Preparation kernels: weight transpose (+ bf16 -> fp16 conversion) so that
-// both MFMA operands of the projections are K-contiguous, and the key extent
-// of a padding mask.
+// both MFMA operands of the projections are K-contiguous, and the scan of a
+// padding mask (key extent and per-tile ignore bits of each batch element),
+// in one launch; then the batch elements ranked by key extent.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -10,16 +11,46 @@ namespace {
 
 constexpr int TT = 64;   // transpose tile edge
 
-// WT[n][k] = W[k][n] for up to two matrices in one launch (the first
-// `tiles0` workgroups take the first, the rest the second); one 64 x 64 tile
-// per workgroup, 256 threads. Global traffic moves 16 bytes per lane both
-// ways: rows of W are read as 8-element chunks, and each output chunk gathers
-// 8 consecutive k of one column from LDS (rows padded by 16 bytes, so the 8
-// lanes gathering one column chunk hit different banks). Requires K and N to
-// be multiples of 8.
+// One launch: workgroups [0, tiles_t) transpose weights, WT[n][k] = W[k][n]
+// for up to two matrices (the first `tiles0` workgroups take the first), one
+// 64 x 64 tile each; workgroups past them scan the padding mask of one batch
+// element each.
+//
+// Transpose: global traffic moves 16 bytes per lane both ways: rows of W are
+// read as 8-element chunks, and each output chunk gathers 8 consecutive k of
+// one column from LDS (rows padded by 16 bytes, so the 8 lanes gathering one
+// column chunk hit different banks). Requires K and N to be multiples of 8.
+//
+// Mask scan: each wave takes 64-key tiles in turn, one key per lane; the
+// wave's ballot of "ignored" (masked or past T_k) is the tile's 64-bit ignore
+// mask, and its highest clear bit the tile's last unmasked key. kend[b] = 1 +
+// the last unmasked key, 0 if every key is masked.
 __global__ void __launch_bounds__(256)
-transpose_bf16_kernel(TransposeJob j0, TransposeJob j1, int tiles0) {
+prep_kernel(TransposeJob j0, TransposeJob j1, int tiles0, int tiles_t, MaskScan ms) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[TT][TT + 8];
+  __shared__ int red[4];
+  if ((int)blockIdx.x >= tiles_t) {
+    const int b = (int)blockIdx.x - tiles_t;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int T_k = ms.T_k, ntk = (T_k + 63) / 64;
+    const uint8_t* mrow = ms.mask + (size_t)b * T_k;
+    int last = -1;
+    for (int t = wave; t < ntk; t += 4) {
+      const int key = t * 64 + lane;
+      const bool ign = key >= T_k || mrow[key] != 0;
+      const uint64_t ib = __ballot(ign);
+      if (lane == 0) {
+        ms.bits[((size_t)b * ntk + t) * 2] = (uint32_t)ib;
+        ms.bits[((size_t)b * ntk + t) * 2 + 1] = (uint32_t)(ib >> 32);
+      }
+      const uint64_t keep = ~ib;
+      if (keep) last = t * 64 + 63 - __builtin_clzll(keep);   // tiles rise per wave
+    }
+    if (lane == 0) red[wave] = last;
+    __syncthreads();
+    if (threadIdx.x == 0) ms.kend[b] = max(max(red[0], red[1]), max(red[2], red[3])) + 1;
+    return;
+  }
   const bool second = (int)blockIdx.x >= tiles0;
   const TransposeJob& jb = second ? j1 : j0;
   const int blk = second ? (int)blockIdx.x - tiles0 : (int)blockIdx.x;
@@ -56,19 +87,6 @@ transpose_bf16_kernel(TransposeJob j0, TransposeJob j1, int tiles0) {
 }
 
 // One workgroup per batch element: largest unmasked key index + 1.
-__global__ void __launch_bounds__(256)
-mask_extent_kernel(const uint8_t* __restrict__ mask, int T_k, int* __restrict__ kend) {
-  __shared__ int red[4];
-  const int b = blockIdx.x;
-  int last = -1;
-  for (int j = threadIdx.x; j < T_k; j += 256)
-    if (mask[(size_t)b * T_k + j] == 0) last = j;
-  for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = last;
-  __syncthreads();
-  if (threadIdx.x == 0) kend[b] = max(max(red[0], red[1]), max(red[2], red[3])) + 1;
-}
-
 // Rank of each batch element by key extent (descending, ties by index); every
 // workgroup stages all B extents in LDS and ranks 256 of them. B <= 1024.
 __global__ void __launch_bounds__(256)
@@ -90,11 +108,13 @@ static int transpose_tiles(const TransposeJob& j) {
   return ((j.N + TT - 1) / TT) * ((j.K + TT - 1) / TT);
 }
 
-hipError_t launch_transpose_bf16(const TransposeJob& j0, const TransposeJob* j1, hipStream_t s) {
+hipError_t launch_prep(const TransposeJob& j0, const TransposeJob* j1, const MaskScan& ms,
+                       hipStream_t s) {
   const long long t0 = transpose_tiles(j0), t1 = j1 ? transpose_tiles(*j1) : 0;
-  if (t0 + t1 < 1 || t0 + t1 > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(t0 + t1)), dim3(256), 0, s, j0,
-                     j1 ? *j1 : j0, (int)t0);
+  const long long nb = ms.mask ? ms.B : 0;
+  if (t0 + t1 < 1 || t0 + t1 + nb > 0x7fffffffLL || (ms.mask && ms.T_k < 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(t0 + t1 + nb)), dim3(256), 0, s, j0,
+                     j1 ? *j1 : j0, (int)t0, (int)(t0 + t1), ms);
   return hipGetLastError();
 }
 
@@ -104,9 +124,5 @@ hipError_t launch_mask_order(const int* kend, int B, int* order, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_mask_extent(const uint8_t* mask, int B, int T_k, int* kend, hipStream_t s) {
-  hipLaunchKernelGGL(mask_extent_kernel, dim3(B), dim3(256), 0, s, mask, T_k, kend);
-  return hipGetLastError();
-}
 
 }  // namespace mha
