@@ -25,12 +25,16 @@
 // One wave's work per key tile: NQ x 32 query rows x 64 keys.
 //   S^T = K . Q^T with v_mfma_f32_32x32x16_f16: the K tile is the A operand
 //   (from LDS), Q^T the B operand (held in registers for the whole kernel).
-//   The result puts one query per lane column, so the row max and row sum
-//   over keys are reductions inside a lane plus one exchange with lane l^32.
+//   The result puts one query per lane column, so the row max over keys is a
+//   reduction inside a lane plus one exchange with lane l^32.
 //   O^T += V^T . P^T: P^T is repacked from the S^T accumulators in registers
 //   (fp16, round to nearest even) and used directly as the B operand. V^T
 //   rows are stored with each 16-key group ordered {0-3, 8-11, 4-7, 12-15},
 //   so the keys a lane half needs for one k-step form one 16-byte chunk.
+//   Row sums of P go to the matrix cores too (VALU issue, not MFMA, is the
+//   scarcer resource here): ones . P^T with v_mfma_f32_16x16x32_f16, whose A
+//   operand is a lane selector (below), sums exactly the fp16 weights that
+//   the P . V product uses.
 //
 // Data movement: K and V^T tiles (and, with a padding mask, the tile's 64-bit
 // ignore mask) go from global memory straight into LDS with
@@ -329,13 +333,24 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   }
 
   f32x16_t o[NQ][DT];
-  float base[NQ], l_run[NQ];
+  float base[NQ];
+  f32x4_t lacc[NQ];
+  // Row sums by MFMA. Fed as the B operand of a 16x16x32 product, the P^T
+  // fragment of lane l becomes column l % 16, k-group l / 16: lanes n and
+  // n+32 carry query n, lanes n+16 and n+48 query n+16. The A operand is ones
+  // at row 0 for k-groups 0 and 2 and at row 1 for k-groups 1 and 3, zero
+  // elsewhere (the k map is the same for A and B), so D[0][n] accumulates the
+  // row sum of query n and D[1][n] that of query n+16: lane n, elements 0, 1.
+  const bool selr = ((lane & 15) == 0 && ((lane >> 4) & 1) == 0) ||
+                    ((lane & 15) == 1 && ((lane >> 4) & 1) == 1);
+  const uint32_t selw = selr ? 0x3c003c00u : 0u;
+  const u32x4 sel = u32x4{selw, selw, selw, selw};
   bool seen[NQ];   // has this lane's query met an unmasked key yet
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
     base[qi] = 0.0f;
     seen[qi] = false;
-    l_run[qi] = 0.0f;
+    lacc[qi] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -479,7 +494,10 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[qi][kh][r] -= shift;
-        l_run[qi] *= alpha;
+        // lane n < 16 holds the sums of queries n and n + 16
+        const float ahi = __shfl(alpha, (lane & 15) | 16);
+        lacc[qi][0] *= alpha;
+        lacc[qi][1] *= ahi;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -488,19 +506,16 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       }
       seen[qi] = seen[qi] || first;
 
-      // Row sum as a tree per fragment group (short dependency depth).
-      float rs4[4];
+      // P = exp2(S') rounded to fp16: the B operand of P . V and of the row sum.
       u32x4 pf[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[qi][c >> 1][(c & 1) * 8 + e]);
-        rs4[c] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pf[c] = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]),
                       pack_f16x2(p[4], p[5]), pack_f16x2(p[6], p[7])};
       }
-      l_run[qi] += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
 
       // P^T fragment c covers keys c*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}; V^T
       // row d supplies the same keys as its chunk 2c + lh.
@@ -508,13 +523,19 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int c = 0; c < 4; ++c) o[qi][dt] = mfma32x32x16<F16>(vf[dt][c], pf[c], o[qi][dt]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        lacc[qi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, sel),
+                                                          __builtin_bit_cast(half8_t, pf[c]),
+                                                          lacc[qi], 0, 0, 0);
     }
   }
 
   // O = acc / l; head `head` occupies columns [head*DK, (head+1)*DK) of (B, T_q, D).
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
-    const float lt = pair32_sum(l_run[qi]);
+    const float l0 = __shfl(lacc[qi][0], lq & 15), l1 = __shfl(lacc[qi][1], lq & 15);
+    const float lt = lq < 16 ? l0 : l1;
     const float inv = 1.0f / lt;
     const int row = qw0 + qi * 32 + lq;
     if (row < a.T_q) {
