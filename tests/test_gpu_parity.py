@@ -195,6 +195,90 @@ def test_interior_mask_holes(lib):
     assert rel_err(run_gpu(lib, w, inp), oracle_full(inp)) <= TOL["bf16"]
 
 
+# Inputs reshaped so the online softmax leaves its common case: the kernel
+# keeps a row's reference at 0 while its first tile's maximum lies in [0, 8]
+# (log2 units) and otherwise moves it to that maximum, and afterwards moves it
+# whenever a score exceeds it by more than 8. The synthetic workloads' scores
+# stay within about 4, so these cases scale them: "scale" multiplies the
+# inputs by 3 (first maxima above 8), "grow" multiplies position t by
+# 1 + t/96 (rows start at reference 0 and move later), "negative" adds +a to
+# the Q bias and -a to the K bias, which lowers every score of a query by the
+# same amount (first maxima below 0; the attention output is unchanged).
+def _reshape_inputs(w, inp, how):
+    inp = dict(inp)
+    if how == "scale":
+        for k in ("x_q", "x_kv"):
+            if inp[k] is not None:
+                inp[k] = (inp[k].float() * 3.0).to(inp[k].dtype)
+    elif how == "grow":
+        for k in ("x_q", "x_kv"):
+            if inp[k] is not None:
+                t = inp[k].shape[1]
+                fac = (1.0 + torch.arange(t, dtype=torch.float32) / 96.0).view(1, t, 1)
+                inp[k] = (inp[k].float() * fac).to(inp[k].dtype)
+    else:
+        b = inp["b_qkv"].float().clone()
+        b[:w.D] += 1.5
+        b[w.D:2 * w.D] -= 1.5
+        inp["b_qkv"] = b.to(inp["b_qkv"].dtype)
+    return inp
+
+
+def _score_regime(w, inp):
+    """Per (b, head, row): the maximum score over the first 64 keys and over
+    all keys, in log2 units, float64, for the rows the fp16 kernel evaluates
+    (rows >= 64 under the causal mask). Masked keys excluded."""
+    f = as_float64_numpy
+    x_q = f(inp["x_q"])
+    x_kv = f(inp["x_kv"]) if inp["x_kv"] is not None else x_q
+    W_, b_ = f(inp["w_qkv"]), f(inp["b_qkv"])
+    D, h = w.D, w.h
+    dk = D // h
+    q = (x_q @ W_[:, :D] + b_[:D]).reshape(w.B, w.T_q, h, dk).transpose(0, 2, 1, 3)
+    k = (x_kv @ W_[:, D:2 * D] + b_[D:2 * D]).reshape(w.B, w.T_k, h, dk).transpose(0, 2, 1, 3)
+    s = q @ k.transpose(0, 1, 3, 2) * (math.log2(math.e) / math.sqrt(dk))
+    if inp["causal"]:
+        s = np.where(np.triu(np.ones((w.T_q, w.T_k), bool), 1), -np.inf, s)
+    if inp["key_padding_mask"] is not None:
+        s = np.where(_np_mask(inp)[:, None, None, :], -np.inf, s)
+    r0 = 64 if inp["causal"] else 0
+    return s[:, :, r0:, :64].max(-1), s[:, :, r0:, :].max(-1)
+
+
+REF_PATHS = [
+    ("scale, causal d_k=64", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=2, T_q=300, T_k=300),
+     "scale"),
+    ("scale, causal d_k=128", W["causal_bf16_d4096_h32_b1_t8192"],
+     dict(D=1024, h=8, B=2, T_q=300, T_k=300), "scale"),
+    ("grow, causal d_k=64", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=2, T_q=300, T_k=300),
+     "grow"),
+    ("grow, cross padded", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
+     dict(B=3, T_q=200, T_k=333, padding=(100, 333)), "grow"),
+    ("negative, causal d_k=64", W["causal_bf16_d1024_h16_b8_t4096"],
+     dict(B=2, T_q=300, T_k=300), "negative"),
+]
+
+
+@pytest.mark.parametrize("name,base,kw,how", REF_PATHS, ids=[r[0] for r in REF_PATHS])
+def test_softmax_reference_paths(lib, name, base, kw, how):
+    w = base.shrink(name=name, **kw)
+    _say(f"[parity] {name}: {w}")
+    inp = _reshape_inputs(w, make_inputs(w, seed=9), how)
+    first, full = _score_regime(w, inp)
+    ok = np.isfinite(first)
+    if how == "scale":
+        assert np.mean(first[ok] > 8) > 0.25
+    elif how == "grow":
+        assert np.mean((first[ok] >= 0) & (first[ok] <= 8)) > 0.2
+        assert np.mean(full[ok] - np.maximum(first[ok], 0) > 8) > 0.05
+    else:
+        assert np.all(first[ok] < 0)
+    y = run_gpu(lib, w, inp)
+    err = rel_err(y, oracle_full(inp))
+    _say(f"[parity] {name}: err/rms = {err:.3e} (tol {TOL['bf16']})")
+    assert err <= TOL["bf16"]
+
+
 def test_deterministic_and_null_bias_equals_zero_bias(lib):
     w = W["causal_bf16_d512_h8_b16_t1024"].shrink(B=2, T_q=333, T_k=333)
     _say(f"[parity] determinism / null bias: {w}")

@@ -9,11 +9,14 @@
 // numerator sum_j exp2(s_j - base) v_j and denominator sum_j exp2(s_j - base)
 // are carried across tiles, and both are multiplied by exp2(base_old -
 // base_new) when the reference moves. Any reference gives the same softmax
-// in exact arithmetic (the factor exp2(-base) cancels). The reference is the
-// first tile's row maximum and afterwards moves only when a score exceeds it
-// by more than 8 (log2 units), so exponentials stay in [0, 256] and most
-// tiles need no rescaling. Scores are produced in log2 units: Q is stored
-// pre-multiplied by log2(e)/sqrt(d_k), and the S accumulator starts at -base.
+// in exact arithmetic (the factor exp2(-base) cancels). The reference stays
+// 0 if the first tile's row maximum lies in [0, 8] (log2 units), else it
+// becomes that maximum; afterwards it moves only when a score exceeds it by
+// more than 8. Either way the exponentials stay in [0, 256] and the largest
+// weight seen is at least 1, and most tiles need no rescaling. Scores are
+// produced in log2 units: Q is stored pre-multiplied by log2(e)/sqrt(d_k), and
+// the S accumulator starts at -base, or at the MFMA's constant 0 (no register
+// initialisation) while every row of the wave still has reference 0.
 //
 // Masks: key j > query i under the causal mask and keys flagged in the
 // padding mask (nonzero = ignore) get -inf, so their weight is exactly 0
@@ -346,10 +349,12 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   const uint32_t selw = selr ? 0x3c003c00u : 0u;
   const u32x4 sel = u32x4{selw, selw, selw, selw};
   bool seen[NQ];   // has this lane's query met an unmasked key yet
+  bool moved[NQ];  // wave-uniform: has any lane's reference left 0
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
     base[qi] = 0.0f;
     seen[qi] = false;
+    moved[qi] = false;
     lacc[qi] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -425,14 +430,24 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       const int q_lo = qw0 + qi * 32;
       live[qi] = !(a.causal && k0 > q_lo + 31);
       if (!live[qi]) continue;
-      const float init = -base[qi];
+      if (moved[qi]) {
+        const float init = -base[qi];
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
+        for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[qi][kh][r] = init;
+          for (int r = 0; r < 16; ++r) s[qi][kh][r] = init;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-          s[qi][kh] = mfma32x32x16<F16>(kf[kh][ks], qreg[qi][ks], s[qi][kh]);
+          for (int ks = 0; ks < KSTEPS; ++ks)
+            s[qi][kh] = mfma32x32x16<F16>(kf[kh][ks], qreg[qi][ks], s[qi][kh]);
+        }
+      } else {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          s[qi][kh] = mfma32x32x16<F16>(kf[kh][0], qreg[qi][0], f32x16_t{});
+#pragma unroll
+          for (int ks = 1; ks < KSTEPS; ++ks)
+            s[qi][kh] = mfma32x32x16<F16>(kf[kh][ks], qreg[qi][ks], s[qi][kh]);
+        }
       }
     }
     // (The V^T reads stay behind the score MFMAs: they are part of the
@@ -487,7 +502,8 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       }
       float mx = pair32_max(vmax2(m2[0], m2[1]));
       const bool first = !seen[qi] && mx != -INFINITY;
-      const float shift = first ? mx : (mx > 8.0f ? mx : 0.0f);
+      const float shift = first ? ((mx >= 0.0f && mx <= 8.0f) ? 0.0f : mx)
+                                : (mx > 8.0f ? mx : 0.0f);
       if (__ballot(shift != 0.0f)) {
         const float alpha = seen[qi] ? __builtin_amdgcn_exp2f(-shift) : 1.0f;
 #pragma unroll
@@ -503,6 +519,7 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[qi][dt][r] *= alpha;
         base[qi] += shift;
+        moved[qi] = true;
       }
       seen[qi] = seen[qi] || first;
 
