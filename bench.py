@@ -52,6 +52,9 @@ KERNEL_SOURCES = {
                   "transformer_head_attention_amd/csrc/device_common.h"],
     "decode_attention": ["transformer_head_attention_amd/csrc/decode.hip",
                          "transformer_head_attention_amd/csrc/device_common.h"],
+    # the QKV projection's GEMM launches (their bytes are summed per step)
+    "qkv_proj": ["transformer_head_attention_amd/csrc/gemm16.hip",
+                 "transformer_head_attention_amd/csrc/device_common.h"],
 }
 
 
