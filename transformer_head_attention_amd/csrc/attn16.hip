@@ -54,9 +54,11 @@ namespace mha {
 
 namespace {
 
-// K and V bytes a group of interleaved causal units may span: one XCD's L2.
+// K and V bytes a group of interleaved causal units may span: twice one
+// XCD's 4 MiB L2. What no longer fits the L2 is refetched from the Infinity
+// Cache; the longer groups balance the causal schedule better than that costs.
 #ifndef MHA_ATTN_GROUP_BYTES
-#define MHA_ATTN_GROUP_BYTES (4LL << 20)
+#define MHA_ATTN_GROUP_BYTES (8LL << 20)
 #endif
 constexpr int BLOCK_N = 64;   // keys per tile
 constexpr int NWAVES = 4;
@@ -620,8 +622,8 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
   const int total = (a.Tqp / bm) * a.h * a.B;
   // Causal, unpadded: query blocks of groups of G units are interleaved
   // longest first. G keeps the group's K and V (4 Tkp d_k bytes per key/value
-  // set, shared by h / h_kv heads) within one XCD's L2, at most 16 and at
-  // most the units one XCD runs.
+  // set, shared by h / h_kv heads) within MHA_ATTN_GROUP_BYTES, at most 16 and
+  // at most the units one XCD runs.
   AttnF16Args ag = a;
   ag.group_units = 1;
   if (a.causal && !a.mbits) {
