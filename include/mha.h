@@ -56,9 +56,10 @@
  *     workspaces differ and no profiling is active.
  *
  * Supported on the GPU: d_k = D / h in {64, 128}, D a multiple of 128,
- * n_g dividing h, B, T_q, T_k >= 1. fp16 overflow bound: every projected
- * Q, K, V value and every attention output must stay below 65504 in
- * magnitude (bf16 path).
+ * n_g dividing h, B, T_q, T_k >= 1. fp16 range (bf16 path, which holds W_O
+ * and the intermediates in fp16): every W_O entry, every projected Q, K, V
+ * value and every attention output must stay below 65504 in magnitude; a
+ * larger one becomes +-inf and propagates into y without an error status.
  */
 #ifndef MHA_H
 #define MHA_H

@@ -15,5 +15,6 @@ pages state); none is "parity unpinned".
 
 from .mha_oracle import (  # noqa: F401
     linear, split_heads, concat_heads, masked_scores, softmax_rows,
-    attention, mha_forward, mha_forward_rows, param_count,
+    attention, mha_forward, mha_forward_rows, mha_forward_blocked, param_count,
+    sigmoid, head_gates, apply_gates,
 )

@@ -14,6 +14,8 @@ library and no max-shift, so it shares no arithmetic shape with
 * With n_g key/value sets (itwiki, 추론 비용과 변형, variants table), query
   head i takes its keys and values from set i // (h / n_g): columns
   D + g*d_k ... of the K block and D + n_g*d_k + g*d_k ... of the V block.
+* Gated attention (same itwiki section, last paragraph): head i's o_i is
+  multiplied by 1 / (1 + exp(-z)), z = x_q . W_G[:, i] + b_G[i].
 """
 
 from __future__ import annotations
@@ -34,8 +36,16 @@ def _matvec(x, w, col0, ncol, b):
     return out
 
 
+def _gate(z):
+    """Logistic function of a Python float, without overflow for large |z|."""
+    if z >= 0.0:
+        return 1.0 / (1.0 + math.exp(-z))
+    e = math.exp(z)
+    return e / (1.0 + e)
+
+
 def brute_force_mha(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
-                    key_padding_mask=None, n_kv_heads=None):
+                    key_padding_mask=None, n_kv_heads=None, gate_w=None, gate_b=None):
     """Nested lists in, nested list Y[b][t][c] out. Inputs are plain floats."""
     D = len(w_qkv)
     d = D // h
@@ -74,6 +84,11 @@ def brute_force_mha(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
                     o = [float("nan")] * d
                 else:
                     o = [oc / total for oc in o]
+                if gate_w is not None:
+                    z = sum(x_q[b][i][r] * gate_w[r][head] for r in range(D))
+                    if gate_b is not None:
+                        z += gate_b[head]
+                    o = [oc * _gate(z) for oc in o]
                 o_cat.extend(o)
             y_b.append(_matvec(o_cat, w_o, 0, D, b_o))
         y_all.append(y_b)

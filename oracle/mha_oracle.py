@@ -35,6 +35,9 @@ Sources (pages as titled; sections / equations named, no line numbers):
   autoregressive generation the keys and values of earlier tokens are kept in
   a KV cache, so a step computes only the new tokens' projections and reads
   every cached key and value.
+* Same itwiki section, last paragraph (gated attention): the scaled
+  dot-product attention output of each head is multiplied by a sigmoid gate
+  of its own.
 
 Conventions (readings where the pages leave a step open):
 
@@ -49,6 +52,12 @@ Conventions (readings where the pages leave a step open):
   plain multi-head attention, n_g = 1 multi-query attention.
 * The scale is 1/sqrt(d_k) (one page prints QK^T/d_k; every other statement,
   including the variance argument of §8 on iamjaehka13.blog, has the root).
+* Gated attention (the page does not say what the gate is computed from):
+  one gate value per batch element, query position and head, from the
+  query-side input like the projections, sigma(x_q . W_G + b_G) with W_G of
+  shape (D, h) and b_G of shape (h,); head i's output O_i (the weighted sum
+  of its values) is multiplied by column i of it before the concat. Without
+  W_G there is no gate.
 * softmax subtracts the row maximum before exponentiating. In exact
   arithmetic this changes nothing (the factor exp(-max) cancels); it only
   keeps exp() in range. A row with every key masked is 0/0 = NaN.
@@ -120,6 +129,24 @@ def attention(q, k, v, causal=False, key_padding_mask=None, q_pos=None):
     return a @ v, a
 
 
+def sigmoid(x):
+    """1 / (1 + exp(-x)); for very negative x, exp overflows to inf and the
+    result is 1/inf = 0."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+
+
+def head_gates(x_q, gate_w, gate_b) -> np.ndarray:
+    """Gate of every head at every query position: sigma(x_q . W_G + b_G),
+    (B, T_q, h) for x_q (B, T_q, D), W_G (D, h), b_G (h,) or None."""
+    return sigmoid(linear(x_q, gate_w, gate_b))
+
+
+def apply_gates(o: np.ndarray, gates: np.ndarray) -> np.ndarray:
+    """O (B, h, T, d_v) with head i's rows multiplied by gates (B, T, h)[..., i]."""
+    return o * np.transpose(gates, (0, 2, 1))[..., None]
+
+
 def _as64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
@@ -163,16 +190,19 @@ def _attend_grouped(qh, kh, vh, n_g, causal, mask, q_pos=None):
 
 def mha_forward(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
                 key_padding_mask=None, return_intermediates=False, n_kv_heads=None,
-                residual=False):
+                residual=False, gate_w=None, gate_b=None):
     """Y = Concat(head_1..head_h) W^O + b_O for batch-first inputs.
 
     x_q (B, T_q, D); x_kv (B, T_k, D) or None for self-attention;
     w_qkv (D, D + 2 n_g d_k) (3D wide for n_kv_heads None = h);
     b_qkv (D + 2 n_g d_k,) or None; w_o (D, D); b_o (D,) or None;
     key_padding_mask (B, T_k), nonzero = ignore, or None. ``residual`` adds
-    x_q to the result. Everything is evaluated in float64.
+    x_q to the result. ``gate_w`` (D, h) and ``gate_b`` (h,) or None: gated
+    attention, head i's output times sigma(x_q . W_G + b_G)[..., i].
+    Everything is evaluated in float64.
     """
     x_q, x_kv, w_qkv, b_qkv, w_o, b_o = map(_as64, (x_q, x_kv, w_qkv, b_qkv, w_o, b_o))
+    gate_w, gate_b = _as64(gate_w), _as64(gate_b)
     B, T_q, D = x_q.shape
     if D % h != 0:
         raise ValueError("embed_dim must be divisible by num_heads")
@@ -183,6 +213,8 @@ def mha_forward(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
     qh = split_heads(q, h)
     kh, vh = split_heads(k, n_g), split_heads(v, n_g)
     o, a = _attend_grouped(qh, kh, vh, n_g, causal, key_padding_mask)
+    if gate_w is not None:
+        o = apply_gates(o, head_gates(x_q, gate_w, gate_b))
     o_cat = concat_heads(o)
     y = linear(o_cat, w_o, b_o)
     if residual:
@@ -206,7 +238,8 @@ def attention_weights(x_q, w_qkv, b_qkv, h, x_kv=None, causal=False, key_padding
 
 
 def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
-                     causal=False, key_padding_mask=None, n_kv_heads=None, residual=False):
+                     causal=False, key_padding_mask=None, n_kv_heads=None, residual=False,
+                     gate_w=None, gate_b=None):
     """Y[b, t, :] for selected query rows only.
 
     ``rows`` maps a batch index b to a 1-D array of query positions t. The
@@ -216,6 +249,7 @@ def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
     Returns {b: (len(rows[b]), D) float64 array}.
     """
     w_qkv, b_qkv, w_o, b_o = map(_as64, (w_qkv, b_qkv, w_o, b_o))
+    gate_w, gate_b = _as64(gate_w), _as64(gate_b)
     D = w_qkv.shape[0]
     n_g = _kv_width(w_qkv, D, h, n_kv_heads)
     d_kv = n_g * (D // h)
@@ -233,10 +267,64 @@ def mha_forward_rows(x_q, w_qkv, b_qkv, w_o, b_o, h, rows, x_kv=None,
         qh = split_heads(q, h)
         kh, vh = split_heads(k, n_g), split_heads(v, n_g)
         o, _ = _attend_grouped(qh, kh, vh, n_g, causal, mask_b, q_pos=ts)
+        if gate_w is not None:
+            o = apply_gates(o, head_gates(xq_b, gate_w, gate_b))
         out[b] = linear(concat_heads(o), w_o, b_o)[0]
         if residual:
             out[b] = xq_b[0] + out[b]
     return out
+
+
+def mha_forward_blocked(x_q, w_qkv, b_qkv, w_o, b_o, h, x_kv=None, causal=False,
+                        key_padding_mask=None, n_kv_heads=None, residual=False,
+                        gate_w=None, gate_b=None, rows_per_block=256, progress=None,
+                        map_blocks=map):
+    """The whole of ``mha_forward``'s Y, evaluated one batch element and one
+    block of query rows at a time so that the score tensor held at once is
+    (h, rows_per_block, T_k) instead of (B, h, T_q, T_k).
+
+    The same steps as ``mha_forward``: per batch element the fused projection
+    of all its rows (Q from x_q, K and V from x_kv or x_q), the head split,
+    then per block of query rows the masked scores at those rows' positions,
+    the row softmax, the weighted sum, the concat and W_O. Rows are
+    independent, so every row equals that row of ``mha_forward``, whatever
+    order the blocks are evaluated in: ``map_blocks`` (default the builtin
+    map) may evaluate them concurrently, e.g. a thread pool's map.
+    ``progress(b, t0, t1)`` is called after each block, if given.
+    """
+    w_qkv, b_qkv, w_o, b_o = map(_as64, (w_qkv, b_qkv, w_o, b_o))
+    gate_w, gate_b = _as64(gate_w), _as64(gate_b)
+    B, T_q, D = x_q.shape
+    if D % h != 0:
+        raise ValueError("embed_dim must be divisible by num_heads")
+    if causal and x_kv is not None and x_kv.shape[1] != T_q:
+        raise ValueError("causal mask needs T_q == T_k")
+    n_g = _kv_width(w_qkv, D, h, n_kv_heads)
+    y = np.empty((B, T_q, D), dtype=np.float64)
+    for b in range(B):
+        xq_b = _as64(x_q[b])[None]
+        xkv_b = None if x_kv is None else _as64(x_kv[b])[None]
+        q, k, v = _qkv(xq_b, xkv_b, w_qkv, b_qkv, D)
+        qh = split_heads(q, h)
+        kh, vh = split_heads(k, n_g), split_heads(v, n_g)
+        mask_b = None if key_padding_mask is None else np.asarray(key_padding_mask)[b:b + 1]
+
+        def rows_block(t0, qh=qh, kh=kh, vh=vh, mask_b=mask_b, xq_b=xq_b):
+            t1 = min(T_q, t0 + rows_per_block)
+            o, _ = _attend_grouped(qh[:, :, t0:t1], kh, vh, n_g, causal, mask_b,
+                                   q_pos=np.arange(t0, t1))
+            if gate_w is not None:
+                o = apply_gates(o, head_gates(xq_b[:, t0:t1], gate_w, gate_b))
+            yb = linear(concat_heads(o), w_o, b_o)[0]
+            if residual:
+                yb = xq_b[0, t0:t1] + yb
+            return t0, t1, yb
+
+        for t0, t1, yb in map_blocks(rows_block, range(0, T_q, rows_per_block)):
+            y[b, t0:t1] = yb
+            if progress is not None:
+                progress(b, t0, t1)
+    return y
 
 
 def mha_decode(x_new, w_qkv, b_qkv, w_o, b_o, h, k_cache, v_cache, cache_len,

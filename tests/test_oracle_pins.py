@@ -4,6 +4,7 @@ Each test ties the oracle to a fact the pages fix, a closed form, brute force,
 or an independent library routine (torch.nn.MultiheadAttention in float64).
 """
 
+import concurrent.futures
 import math
 import os
 
@@ -349,6 +350,67 @@ def test_rows_function_equals_full_forward_rows():
                                   rows, x_kv=p["x_kv"], causal=causal, key_padding_mask=mask)
         for b, ts in rows.items():
             assert _rel_err(got[b], y[b, ts]) <= 1e-12
+
+
+@pytest.mark.parametrize("rows_per_block", [1, 3, 7, 64])
+def test_blocked_function_equals_full_forward(rows_per_block):
+    """The row-blocked evaluation used for full-size comparisons returns the
+    whole of mha_forward's Y (NaN rows included), for self/cross, causal,
+    padded (leading, interior and all-masked rows), grouped and residual."""
+    rng = np.random.default_rng(40 + rows_per_block)
+    cases = []
+    p = _rand_problem(rng, 3, 20, 32, 4)
+    mask = np.zeros((3, 20), dtype=np.uint8)
+    mask[0, :5] = 1            # leading keys: causal rows 0..4 see none -> NaN
+    mask[1, 7:12] = 1
+    cases.append((p, True, mask, {}))
+    p = _rand_problem(rng, 2, 11, 32, 4, Tk=17, cross=True)
+    mask = np.zeros((2, 17), dtype=np.uint8)
+    mask[1, :] = 1             # every key of batch element 1 ignored
+    cases.append((p, False, mask, dict(residual=True)))
+    p = _rand_problem(rng, 2, 13, 32, 4)
+    d_k = 8
+    p["w_qkv"] = rng.standard_normal((32, 32 + 2 * 2 * d_k)) / math.sqrt(32)
+    p["b_qkv"] = rng.standard_normal(32 + 2 * 2 * d_k) * 0.1
+    cases.append((p, True, None, dict(n_kv_heads=2)))
+    for p, causal, mask, kw in cases:
+        y = _run(p, 4, causal, mask, **kw)
+        calls = []
+        got = mo.mha_forward_blocked(p["x_q"], p["w_qkv"], p["b_qkv"], p["w_o"], p["b_o"], 4,
+                                     x_kv=p["x_kv"], causal=causal, key_padding_mask=mask,
+                                     rows_per_block=rows_per_block,
+                                     progress=lambda b, t0, t1: calls.append((b, t0, t1)), **kw)
+        assert np.array_equal(np.isnan(got), np.isnan(y))
+        ok = ~np.isnan(y)
+        assert _rel_err(got[ok], y[ok]) <= 1e-12
+        B, T = y.shape[:2]
+        assert calls[-1] == (B - 1, (T - 1) // rows_per_block * rows_per_block, T)
+        # blocks evaluated concurrently: the same values, bit for bit
+        with concurrent.futures.ThreadPoolExecutor(4) as ex:
+            par = mo.mha_forward_blocked(p["x_q"], p["w_qkv"], p["b_qkv"], p["w_o"], p["b_o"], 4,
+                                         x_kv=p["x_kv"], causal=causal, key_padding_mask=mask,
+                                         rows_per_block=rows_per_block, map_blocks=ex.map, **kw)
+        assert np.array_equal(par, got, equal_nan=True)
+    # the leading-padding case really produced NaN rows
+    assert np.isnan(_run(cases[0][0], 4, True, cases[0][2])[0, :5]).all()
+
+
+def test_blocked_function_matches_brute_force():
+    """Pinned directly too: brute force at T <= 4 (causal + padding, cross)."""
+    rng = np.random.default_rng(48)
+    for cross, causal in ((False, True), (True, False)):
+        Tk = 4 if causal else 3
+        p = _rand_problem(rng, 2, 4, 8, 2, Tk=Tk, cross=cross)
+        mask = np.zeros((2, Tk), dtype=np.uint8)
+        mask[1, 1] = 1
+        got = mo.mha_forward_blocked(p["x_q"], p["w_qkv"], p["b_qkv"], p["w_o"], p["b_o"], 2,
+                                     x_kv=p["x_kv"], causal=causal, key_padding_mask=mask,
+                                     rows_per_block=3)
+        yb = brute_force_mha(
+            p["x_q"].tolist(), p["w_qkv"].tolist(), p["b_qkv"].tolist(), p["w_o"].tolist(),
+            p["b_o"].tolist(), 2, x_kv=None if p["x_kv"] is None else p["x_kv"].tolist(),
+            causal=causal, key_padding_mask=mask.tolist())
+        assert _rel_err(got, yb) <= 1e-12
 
 
 # ------------------------------------------------ planted mistakes are caught

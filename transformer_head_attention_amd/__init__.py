@@ -195,6 +195,7 @@ class MultiHeadAttention:
         _check(st, "mha_create_grouped")
         self.handle = h
         self._ws = None
+        self._uses = []
 
     def close(self):
         if self.handle is not None:
@@ -264,6 +265,9 @@ class MultiHeadAttention:
             key_padding_mask = key_padding_mask.to(torch.uint8)
         if stream is None:
             stream = torch.cuda.current_stream(x_q.device).cuda_stream
+        # buffers allocated here belong to the current stream; when the
+        # kernels run on another one they are recorded on it below
+        self._uses = [out, workspace, key_padding_mask]
         dt = self._tdtype
         args = (self.handle, self._ptr(x_q, dt), self._ptr(x_kv, dt), self._ptr(w_qkv, dt),
                 self._ptr(b_qkv, dt), self._ptr(w_o, dt), self._ptr(b_o, dt), B, T_q, T_k,
@@ -278,7 +282,22 @@ class MultiHeadAttention:
                                        1 if average_weights else 0)
             st = mha_forward_ex(*args, opts, stream)
             _check(st, "mha_forward_ex")
+        self._record(stream, x_q.device)
         return out
+
+    def _record(self, stream, device):
+        """Mark the buffers the call used as in use by `stream` if that is not
+        the current stream: the caching allocator then keeps their memory
+        until the work queued there has finished, even if they are freed (or
+        the cached workspace replaced) on the current stream meanwhile."""
+        torch = self._torch
+        uses, self._uses = self._uses, []
+        if stream == torch.cuda.current_stream(device).cuda_stream:
+            return
+        ext = torch.cuda.ExternalStream(stream, device=device)
+        for t in uses:
+            if t is not None:
+                t.record_stream(ext)
 
     __call__ = forward
 
@@ -314,6 +333,7 @@ class MultiHeadAttention:
             workspace = self._ws
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
+        self._uses = [out, workspace]
         dt = self._tdtype
         st = mha_decode(self.handle, self._ptr(x, dt), self._ptr(w_qkv, dt), self._ptr(b_qkv, dt),
                         self._ptr(w_o, dt), self._ptr(b_o, dt), B, T_new, self._ptr(k_cache, dt),
@@ -321,4 +341,5 @@ class MultiHeadAttention:
                         self._ptr(out, torch.float32), workspace.data_ptr(), workspace.numel(),
                         stream)
         _check(st, "mha_decode")
+        self._record(stream, x.device)
         return out

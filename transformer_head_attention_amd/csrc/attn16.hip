@@ -198,9 +198,9 @@ __device__ __forceinline__ void early_rows_block(const AttnF32Args& a, int blk, 
   }
 }
 
-// d_k = 128: the register budget is capped at two waves per SIMD (a few
-// registers spill); with two pipeline stages (64 KiB of LDS) two workgroups
-// then share a CU, which is faster than one unspilled workgroup.
+// d_k = 128: the register budget is capped at two waves per SIMD (247 VGPRs,
+// no spill); with two pipeline stages (64 KiB of LDS) two workgroups then
+// share a CU.
 template <int DK, int NQ, int NS, bool HAS_MASK>
 __global__ void __launch_bounds__(NT, (DK == 128 ? 2 : 1))
 attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
@@ -263,8 +263,8 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
     if (a.group_units > 1 && a.causal) {
       // Groups of G (batch, head) units: their query blocks interleaved
       // longest first, so the long blocks of the last units of an XCD do not
-      // trail at the end of the launch (G is bounded by the L2 footprint of
-      // the group's K and V).
+      // trail at the end of the launch (G is bounded by MHA_ATTN_GROUP_BYTES
+      // of K and V per group, twice one XCD's L2).
       const int G = a.group_units, units = a.h * a.B;
       const int g0 = (logical / (G * nqb)) * G, gs = min(G, units - g0);
       const int pos = logical - g0 * nqb;
@@ -281,7 +281,8 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   const int bh = b * a.h + head;
   // Key/value set of this query head: consecutive heads share one set, and
   // their workgroups are consecutive in the XCD mappings above, so a set's K
-  // and V are read into one XCD's L2 for the whole group.
+  // and V are read by one XCD; what its L2 cannot hold of a group's K and V
+  // is refetched from the Infinity Cache.
   const int kvh = b * a.h_kv + head / (a.h / a.h_kv);
 
   const uint16_t* Qg = a.q + (size_t)bh * a.Tqp * DK;
@@ -489,10 +490,6 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       }
 
       // Row maximum: two chains of three-input maxima over the 32 scores.
-      // (vmax3 is inline assembly, before which the compiler inserts no wait
-      // states; the V^T fragment reads pinned after the score MFMAs and the
-      // mask branch put well over the 11 that a VALU read of an 8-pass MFMA
-      // result needs between the two.)
       float m2[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {

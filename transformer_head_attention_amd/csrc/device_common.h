@@ -101,19 +101,18 @@ __device__ __forceinline__ float load_bias_bf16(const uint16_t* b, int i) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Maximum of three / two floats as one v_max3_f32 / v_max_f32. fmaxf on
-// values the compiler cannot prove canonical (MFMA results) first
-// canonicalizes each input with an extra v_max_f32 x, x; these take the
-// values as they are (inputs here are never signaling NaNs).
+// Maximum of three / two floats. __builtin_elementwise_maximum (IEEE
+// maximum: a NaN operand gives NaN) lowers to gfx950's v_maximum3_f32, which
+// takes its operands as they are: fmaxf (maxnum) on values the compiler
+// cannot prove canonical, such as MFMA results, first canonicalises each
+// input with an extra v_max_f32 x, x. Being ordinary compiler-visible
+// instructions, these also get the wait states a VALU read of an MFMA result
+// needs from the compiler's hazard recogniser.
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 __device__ __forceinline__ float vmax2(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
+  return __builtin_elementwise_maximum(a, b);
 }
 
 // Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: a VALU

@@ -112,7 +112,35 @@ bool sizes_ok(const mha_handle* hd, int B, int T_q, int T_k) {
   return true;
 }
 
+// Every argument check of the forward pass except the workspace's.
+mha_status_t check_forward_args(const mha_handle* hd, const void* x_q, const void* x_kv,
+                                const void* w_qkv, const void* b_qkv, const void* w_o,
+                                const void* b_o, int B, int T_q, int T_k, int causal,
+                                const void* y, const mha_forward_options* opts) {
+  if (!hd) return MHA_ERR_INVALID_ARG;
+  if (!x_q || !w_qkv || !w_o || !y) return MHA_ERR_INVALID_ARG;
+  const int residual = opts ? opts->residual : 0;
+  const int y_bf16 = opts ? opts->y_bf16 : 0;
+  const float* weights = opts ? opts->attn_weights : nullptr;
+  const int average = opts ? opts->average_weights : 0;
+  if ((residual != 0 && residual != 1) || (y_bf16 != 0 && y_bf16 != 1) ||
+      (average != 0 && average != 1))
+    return MHA_ERR_INVALID_ARG;
+  if (weights && !aligned16(weights)) return MHA_ERR_INVALID_ARG;
+  if (y_bf16 && hd->dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
+  if (weights && (T_k > mha::kWeightsMaxKeys || B > 65535)) return MHA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return MHA_ERR_INVALID_ARG;
+  if (!x_kv && T_k != T_q) return MHA_ERR_INVALID_ARG;
+  if (causal && T_k != T_q) return MHA_ERR_INVALID_ARG;
+  if (!sizes_ok(hd, B, T_q, T_k)) return MHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_q, x_kv, w_qkv, b_qkv, w_o, b_o, y};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MHA_ERR_INVALID_ARG;
+  return MHA_OK;
+}
+
 thread_local hipError_t g_last_hip_error = hipSuccess;
+
 
 // Workspace of one generation step (bf16 handles).
 struct DecodeLayout {
@@ -288,25 +316,14 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
                             int T_k, int causal, const unsigned char* key_padding_mask, void* y,
                             void* workspace, size_t workspace_bytes,
                             const mha_forward_options* opts, void* stream_) {
-  if (!hd) return MHA_ERR_INVALID_ARG;
-  if (!x_q || !w_qkv || !w_o || !y || !workspace) return MHA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return MHA_ERR_INVALID_ARG;
+  const mha_status_t chk = check_forward_args(hd, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k,
+                                              causal, y, opts);
+  if (chk != MHA_OK) return chk;
   const int residual = opts ? opts->residual : 0;
   const int y_bf16 = opts ? opts->y_bf16 : 0;
   float* weights = opts ? opts->attn_weights : nullptr;
   const int average = opts ? opts->average_weights : 0;
-  if ((residual != 0 && residual != 1) || (y_bf16 != 0 && y_bf16 != 1) ||
-      (average != 0 && average != 1))
-    return MHA_ERR_INVALID_ARG;
-  if (weights && !aligned16(weights)) return MHA_ERR_INVALID_ARG;
-  if (y_bf16 && hd->dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
-  if (weights && (T_k > mha::kWeightsMaxKeys || B > 65535)) return MHA_ERR_UNSUPPORTED;
-  if (causal != 0 && causal != 1) return MHA_ERR_INVALID_ARG;
-  if (!x_kv && T_k != T_q) return MHA_ERR_INVALID_ARG;
-  if (causal && T_k != T_q) return MHA_ERR_INVALID_ARG;
-  if (!sizes_ok(hd, B, T_q, T_k)) return MHA_ERR_INVALID_ARG;
-  const void* ptrs[] = {x_q, x_kv, w_qkv, b_qkv, w_o, b_o, y, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return MHA_ERR_INVALID_ARG;
   const Layout L = make_layout(hd, B, T_q, T_k);
   if (workspace_bytes < L.total) return MHA_ERR_WORKSPACE;
 
