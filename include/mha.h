@@ -202,6 +202,35 @@ mha_status_t mha_forward_ex(mha_handle_t handle,
                             const mha_forward_options* opts,
                             void* stream);
 
+/* ---- Forward pass without caller-provided memory -----------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture that must not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation. Same computation, arguments and options as
+ * mha_forward_ex, without the workspace: the scratch comes from a
+ * MHA_NOALLOC_SCRATCH_BYTES array that the library holds in each GPU's
+ * memory from the first call on that GPU until the process ends. No device
+ * memory is allocated or freed by the call.
+ *   - Sizes whose mha_workspace_size() exceeds MHA_NOALLOC_SCRATCH_BYTES are
+ *     rejected with MHA_ERR_WORKSPACE before anything is enqueued.
+ *   - Every call on one GPU uses that GPU's one array (whatever the handle):
+ *     calls that overlap in time on one GPU (different streams, threads or
+ *     processes' graphs replayed concurrently) race and give undefined
+ *     results. Calls on one stream are ordered and safe.
+ *   - The array keeps the last call's contents; nothing in it needs to start
+ *     at zero.
+ * Errors as mha_forward_ex; a failure to look up the array's device address
+ * returns MHA_ERR_HIP. */
+#define MHA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mha_status_t mha_forward_noalloc(mha_handle_t handle,
+                                 const void* x_q, const void* x_kv,
+                                 const void* w_qkv, const void* b_qkv,
+                                 const void* w_o, const void* b_o,
+                                 int B, int T_q, int T_k, int causal,
+                                 const unsigned char* key_padding_mask,
+                                 void* y,
+                                 const mha_forward_options* opts,
+                                 void* stream);
+
 /* Release a handle (NULL is accepted). */
 mha_status_t mha_destroy(mha_handle_t handle);
 

@@ -209,3 +209,37 @@ def test_forward_options_validation(mha):
     finally:
         mha.mha_destroy(h)
         mha.mha_destroy(h32)
+
+
+def test_noalloc_rejects_before_device_work(mha):
+    """mha_forward_noalloc validates like mha_forward and rejects sizes whose
+    workspace exceeds the library's scratch, all before touching a device."""
+    text = open(HEADER).read()
+    m = re.search(r"#define MHA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mha.MHA_NOALLOC_SCRATCH_BYTES
+    st, h = mha.mha_create(1024, 16, mha.MHA_BF16)
+    fake = 1 << 20
+    try:
+        def call(**kw):
+            args = dict(x_q=fake, x_kv=None, w_qkv=fake, b_qkv=None, w_o=fake, b_o=None, B=2,
+                        T_q=16, T_k=16, causal=0, key_padding_mask=None, y=fake, opts=None,
+                        stream=None)
+            args.update(kw)
+            return mha.mha_forward_noalloc(h, *args.values())
+        assert call(x_q=None) == mha.MHA_ERR_INVALID_ARG
+        assert call(causal=3) == mha.MHA_ERR_INVALID_ARG
+        assert call(y=fake + 4) == mha.MHA_ERR_INVALID_ARG
+        # the headline size needs ~272 MiB of workspace
+        assert mha.mha_workspace_size(h, 8, 4096, 4096) > mha.MHA_NOALLOC_SCRATCH_BYTES
+        assert call(B=8, T_q=4096, T_k=4096, causal=1) == mha.MHA_ERR_WORKSPACE
+        # just past the limit, found by bisection on T
+        lo, hi = 1, 4096
+        while lo + 1 < hi:
+            mid = (lo + hi) // 2
+            if mha.mha_workspace_size(h, 2, mid, mid) <= mha.MHA_NOALLOC_SCRATCH_BYTES:
+                lo = mid
+            else:
+                hi = mid
+        assert call(B=2, T_q=hi, T_k=hi) == mha.MHA_ERR_WORKSPACE
+    finally:
+        mha.mha_destroy(h)

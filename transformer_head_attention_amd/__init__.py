@@ -33,8 +33,10 @@ MHA_F32, MHA_BF16 = 0, 1
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP = range(5)
 MHA_NUM_STAGES = 5
 
+MHA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
 EXPORTED = ("mha_create", "mha_create_grouped", "mha_workspace_size", "mha_forward",
-            "mha_forward_ex", "mha_destroy",
+            "mha_forward_ex", "mha_forward_noalloc", "mha_destroy",
             "mha_decode_workspace_size", "mha_decode",
             "mha_status_string", "mha_hip_error_string", "mha_profile_begin", "mha_profile_end",
             "mha_stage_name")
@@ -59,6 +61,9 @@ class mha_forward_options(ctypes.Structure):
 _lib.mha_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
                                 _vp, _vp, _sz, ctypes.POINTER(mha_forward_options), _vp]
 _lib.mha_forward_ex.restype = _int
+_lib.mha_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
+                                     _vp, _vp, ctypes.POINTER(mha_forward_options), _vp]
+_lib.mha_forward_noalloc.restype = _int
 _lib.mha_decode_workspace_size.argtypes = [_vp, _int, _int, _int]
 _lib.mha_decode_workspace_size.restype = _sz
 _lib.mha_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _vp, _vp, _int, _vp, _vp,
@@ -153,6 +158,15 @@ def mha_forward_ex(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k, causa
                                int(T_k), int(causal), key_padding_mask, y, workspace,
                                int(workspace_bytes), None if opts is None else ctypes.byref(opts),
                                stream)
+
+
+def mha_forward_noalloc(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k, causal,
+                        key_padding_mask, y, opts, stream) -> int:
+    """Raw call; ``opts`` is an mha_forward_options or None. No workspace: the
+    library's own per-GPU scratch of MHA_NOALLOC_SCRATCH_BYTES is used."""
+    return _lib.mha_forward_noalloc(handle, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, int(B), int(T_q),
+                                    int(T_k), int(causal), key_padding_mask, y,
+                                    None if opts is None else ctypes.byref(opts), stream)
 
 
 def mha_destroy(handle) -> int:

@@ -1,8 +1,9 @@
 // C ABI of the multi-head attention forward pass (declared in include/mha.h).
 //
-// Host-side only: argument validation, workspace layout and the launch
-// sequence. Every step of the computation runs in the kernels of prep.hip,
-// gemm16.hip, attn16.hip and fp32_path.hip.
+// Host-side code: argument validation, workspace layout and the launch
+// sequence (plus the device-resident scratch array of mha_forward_noalloc).
+// Every step of the computation runs in the kernels of prep.hip, gemm16.hip,
+// attn16.hip and fp32_path.hip.
 //
 // bf16 inputs (stages):
 //   prep       W_QKV -> W_QKV^T (bf16) and W_O -> W_O^T (fp16) so both MFMA
@@ -26,6 +27,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -141,6 +143,33 @@ mha_status_t check_forward_args(const mha_handle* hd, const void* x_q, const voi
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
+// Scratch of mha_forward_noalloc: one copy per GPU, loaded with the code
+// object. Host code never passes `scratch` itself (on the host it only names
+// the symbol): each device's address is looked up once, with that device
+// current, and kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[MHA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // indexed by device ordinal
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device), or the HIP error of the lookup.
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // Workspace of one generation step (bf16 handles).
 struct DecodeLayout {
@@ -555,6 +584,21 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     if (!mark(4) || !mark(5)) return MHA_ERR_HIP;
   }
   return MHA_OK;
+}
+
+mha_status_t mha_forward_noalloc(mha_handle_t hd, const void* x_q, const void* x_kv,
+                                 const void* w_qkv, const void* b_qkv, const void* w_o,
+                                 const void* b_o, int B, int T_q, int T_k, int causal,
+                                 const unsigned char* key_padding_mask, void* y,
+                                 const mha_forward_options* opts, void* stream_) {
+  const mha_status_t chk = check_forward_args(hd, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k,
+                                              causal, y, opts);
+  if (chk != MHA_OK) return chk;
+  if (make_layout(hd, B, T_q, T_k).total > MHA_NOALLOC_SCRATCH_BYTES) return MHA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  MHA_HIP(scratch_ptr(&ws));
+  return mha_forward_ex(hd, x_q, x_kv, w_qkv, b_qkv, w_o, b_o, B, T_q, T_k, causal,
+                        key_padding_mask, y, ws, MHA_NOALLOC_SCRATCH_BYTES, opts, stream_);
 }
 
 size_t mha_decode_workspace_size(mha_handle_t hd, int B, int T_new, int T_max) {
