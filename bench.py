@@ -162,7 +162,8 @@ def cpu_baseline(w, inp, budget_s: float = 10.0):
         mha_oracle.mha_forward(
             f(inp["x_q"][b]), wq, bq, wo, bo, w.h,
             x_kv=None if inp["x_kv"] is None else f(inp["x_kv"][b]), causal=w.causal,
-            key_padding_mask=None if mask is None else mask[b].numpy(), n_kv_heads=w.n_g)
+            key_padding_mask=None if mask is None else mask[b].numpy(), n_kv_heads=w.n_g,
+            gate_w=f(inp["gate_w"]), gate_b=f(inp["gate_b"]))
         spent += time.perf_counter() - t0
         done += 1
     flops = w.flops() / w.B * done
@@ -323,7 +324,8 @@ def main() -> int:
     def step():
         m.forward(t["x_q"], t["w_qkv"], t["w_o"], b_qkv=t["b_qkv"], b_o=t["b_o"], x_kv=t["x_kv"],
                   causal=w.causal, key_padding_mask=t["key_padding_mask"], out=y, workspace=ws,
-                  stream=stream.cuda_stream, residual=args.residual, y_dtype=args.y_dtype)
+                  stream=stream.cuda_stream, residual=args.residual, y_dtype=args.y_dtype,
+                  gate_w=t["gate_w"], gate_b=t["gate_b"])
 
     # Untimed warmup: the first few hundred microseconds of sustained work
     # run at a different clock than the steady state that follows.
@@ -376,7 +378,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "T_q": w.T_q, "T_k": w.T_k, "D": w.D, "h": w.h,
                    "n_kv_heads": w.n_g, "d_k": w.d_k, "causal": w.causal, "cross": w.cross,
-                   "key_padding": w.padding is not None, "gflop_per_step": round(flops / 1e9, 3),
+                   "key_padding": w.padding is not None, "gated": w.gate,
+                   "gflop_per_step": round(flops / 1e9, 3),
                    "intermediates": "fp16 Q/K/V/P/O, fp32 accumulate",
                    "y": args.y_dtype, "residual": args.residual},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_MFMA_16BIT_TFLOPS, 2),

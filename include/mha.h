@@ -181,12 +181,26 @@ mha_status_t mha_decode(mha_handle_t handle, const void* x,
  *                  MHA_ERR_UNSUPPORTED. On the bf16 path the weights come
  *                  from the fp16 Q and K of the computation (relative error
  *                  about 1e-3), on the fp32 path from fp32 Q and K. Recorded
- *                  in the "attention" stage of the timing hooks. */
+ *                  in the "attention" stage of the timing hooks.
+ * gate_w, gate_b   gated attention (itwiki "멀티 헤드 어텐션", 추론 비용과
+ *                  변형, last paragraph: each head's scaled dot-product
+ *                  attention output is multiplied by a sigmoid gate of its
+ *                  own). gate_w NULL: no gate. Otherwise a DEVICE (D, h)
+ *                  matrix of the handle's dtype, row-major, and gate_b a
+ *                  DEVICE (h) vector or NULL (zero), both 16-byte aligned:
+ *                  head i's output at query row t of batch b is multiplied
+ *                  by 1 / (1 + exp(-g)), g = x_q[b, t, :] . gate_w[:, i] +
+ *                  gate_b[i], before the concat and W_O. gate_b without
+ *                  gate_w -> MHA_ERR_INVALID_ARG. The attention weights
+ *                  output is not gated. Recorded in the "qkv_proj" stage.
+ * Zero-initialise the struct (all fields 0 / NULL are the defaults). */
 typedef struct {
   int residual;
   int y_bf16;
   float* attn_weights;
   int average_weights;
+  const void* gate_w;
+  const void* gate_b;
 } mha_forward_options;
 
 /* mha_forward with options (opts may be NULL: the defaults, all zero, are

@@ -32,7 +32,8 @@ design notes):
   workload's dtype; everything downstream sees those rounded values.
 
 Draw order from one CPU ``torch.Generator`` seeded with ``seed``:
-X (or X_q then X_kv), W_QKV, W_O, b_QKV, b_O, then the valid lengths.
+X (or X_q then X_kv), W_QKV, W_O, b_QKV, b_O, then the valid lengths, then
+(gated attention only) W_G and b_G.
 """
 
 from __future__ import annotations
@@ -63,6 +64,7 @@ class Workload:
     weight_std: float = 0.0
     bias_std: Optional[float] = None  # None -> zero biases
     n_kv: Optional[int] = None        # key/value sets n_g (None -> h, plain MHA)
+    gate: bool = False                # gated attention: W_G (D, h), b_G (h)
 
     @property
     def d_k(self) -> int:
@@ -82,12 +84,14 @@ class Workload:
         T_q == T_k) plus 4*T_q*T_k*D for scores and weighted sum, halved
         under a causal mask, per batch element (itwiki, 매개변수와 계산량).
         With n_g key/value sets the K and V projections are n_g d_k wide:
-        4*T_k*D*n_g*d_k instead of 4*T_k*D^2."""
+        4*T_k*D*n_g*d_k instead of 4*T_k*D^2. Gated attention adds the gate
+        projection, 2*T_q*D*h."""
         proj = 4.0 * self.T_q * self.D ** 2 + 4.0 * self.T_k * self.D * self.n_g * self.d_k
         attn = 4.0 * self.T_q * self.T_k * self.D
         if self.causal:
             attn *= 0.5
-        return self.B * (proj + attn)
+        gate = 2.0 * self.T_q * self.D * self.h if self.gate else 0.0
+        return self.B * (proj + attn + gate)
 
     def shrink(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -121,7 +125,16 @@ GROUPED_WORKLOADS = {
                  causal=True, bias_std=0.02, n_kv=1),
     ]
 }
-ALL_WORKLOADS = {**WORKLOADS, **GROUPED_WORKLOADS}
+# Gated attention (itwiki, 추론 비용과 변형, last paragraph) at the d_model =
+# 1024 causal shape: W_G Xavier-uniform (fan_in D, fan_out h), b_G N(0, 0.02).
+GATED_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("gated_causal_bf16_d1024_h16_b8_t4096", "bf16", 1024, 16, 8, 4096, 4096,
+                 causal=True, bias_std=0.02, gate=True),
+    ]
+}
+ALL_WORKLOADS = {**WORKLOADS, **GROUPED_WORKLOADS, **GATED_WORKLOADS}
 
 HEADLINE = "causal_bf16_d1024_h16_b8_t4096"
 
@@ -172,6 +185,11 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         lengths = torch.randint(lo, hi + 1, (w.B,), generator=g)
         j = torch.arange(w.T_k)
         mask = (j[None, :] >= lengths[:, None]).to(torch.uint8)
+    gate_w = gate_b = None
+    if w.gate:
+        # drawn last, so the other inputs equal those of the ungated workload
+        gate_w = _uniform(g, (D, w.h), math.sqrt(6.0 / (D + w.h)))
+        gate_b = torch.zeros(w.h) if w.bias_std is None else _normal(g, (w.h,), w.bias_std)
     dt = torch_dtype(w)
     out = {
         "x_q": x_q.to(dt),
@@ -182,6 +200,8 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         "b_o": b_o.to(dt),
         "key_padding_mask": mask,
         "lengths": lengths,
+        "gate_w": None if gate_w is None else gate_w.to(dt),
+        "gate_b": None if gate_b is None else gate_b.to(dt),
         "h": w.h,
         "n_kv": w.n_g,
         "causal": w.causal,

@@ -54,7 +54,9 @@ def run_gpu(lib, w, inp, stream=None, none_bias=False, mod=None):
                   b_qkv=None if none_bias else _dev(inp["b_qkv"]),
                   b_o=None if none_bias else _dev(inp["b_o"]),
                   x_kv=_dev(inp["x_kv"]), causal=inp["causal"],
-                  key_padding_mask=_dev(inp["key_padding_mask"]), stream=stream)
+                  key_padding_mask=_dev(inp["key_padding_mask"]), stream=stream,
+                  gate_w=_dev(inp.get("gate_w")),
+                  gate_b=None if none_bias else _dev(inp.get("gate_b")))
     torch.cuda.synchronize()
     return y.cpu().double().numpy()
 
@@ -68,7 +70,8 @@ def oracle_full(inp):
     f = as_float64_numpy
     return mo.mha_forward(f(inp["x_q"]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]),
                           f(inp["b_o"]), inp["h"], x_kv=f(inp["x_kv"]), causal=inp["causal"],
-                          key_padding_mask=_np_mask(inp), n_kv_heads=inp["n_kv"])
+                          key_padding_mask=_np_mask(inp), n_kv_heads=inp["n_kv"],
+                          gate_w=f(inp.get("gate_w")), gate_b=f(inp.get("gate_b")))
 
 
 def oracle_rows(inp, rows):
@@ -423,6 +426,7 @@ def oracle_blocked(inp, w, label):
                                       f(inp["w_o"]), f(inp["b_o"]), inp["h"],
                                       x_kv=f(inp["x_kv"]), causal=inp["causal"],
                                       key_padding_mask=_np_mask(inp), n_kv_heads=inp["n_kv"],
+                                      gate_w=f(inp.get("gate_w")), gate_b=f(inp.get("gate_b")),
                                       rows_per_block=rows, progress=progress,
                                       map_blocks=map_blocks)
 

@@ -55,7 +55,8 @@ _lib.mha_forward.restype = _int
 
 class mha_forward_options(ctypes.Structure):
     _fields_ = [("residual", ctypes.c_int), ("y_bf16", ctypes.c_int),
-                ("attn_weights", ctypes.c_void_p), ("average_weights", ctypes.c_int)]
+                ("attn_weights", ctypes.c_void_p), ("average_weights", ctypes.c_int),
+                ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p)]
 
 
 _lib.mha_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
@@ -242,28 +243,32 @@ class MultiHeadAttention:
             raise TypeError(f"expected {dtype}, got {t.dtype}")
         return t.data_ptr()
 
-    def _check_shapes(self, x_q, w_qkv, w_o, b_qkv, b_o, x_kv, key_padding_mask, out):
+    def _check_shapes(self, x_q, w_qkv, w_o, b_qkv, b_o, x_kv, key_padding_mask, out,
+                      gate_w=None, gate_b=None):
         D = self.d_model
         n_qkv = D + 2 * self.num_kv_heads * (D // self.num_heads)
         B, T_q = x_q.shape[0], x_q.shape[1]
         T_k = T_q if x_kv is None else x_kv.shape[1]
         want = [(x_q, (B, T_q, D)), (w_qkv, (D, n_qkv)), (w_o, (D, D)), (b_qkv, (n_qkv,)),
                 (b_o, (D,)), (x_kv, (B, T_k, D)), (key_padding_mask, (B, T_k)),
-                (out, (B, T_q, D))]
+                (out, (B, T_q, D)), (gate_w, (D, self.num_heads)), (gate_b, (self.num_heads,))]
         for t, shape in want:
             if t is not None and tuple(t.shape) != shape:
                 raise ValueError(f"expected shape {shape}, got {tuple(t.shape)}")
 
     def forward(self, x_q, w_qkv, w_o, b_qkv=None, b_o=None, x_kv=None, causal=False,
                 key_padding_mask=None, out=None, workspace=None, stream=None, residual=False,
-                y_dtype="fp32", attn_weights=None, average_weights=False):
+                y_dtype="fp32", attn_weights=None, average_weights=False, gate_w=None,
+                gate_b=None):
         """Returns y. ``residual`` adds x_q; ``y_dtype`` "bf16" stores y as
         bf16; ``attn_weights`` (a (B, h, T_q, T_k) fp32 tensor, or (B, T_q,
-        T_k) with ``average_weights``) receives the softmax weights."""
+        T_k) with ``average_weights``) receives the softmax weights;
+        ``gate_w`` (D, h) and ``gate_b`` (h,) select gated attention."""
         torch = self._torch
         if x_q.dim() != 3:
             raise ValueError("x_q must be (B, T, D)")
-        self._check_shapes(x_q, w_qkv, w_o, b_qkv, b_o, x_kv, key_padding_mask, out)
+        self._check_shapes(x_q, w_qkv, w_o, b_qkv, b_o, x_kv, key_padding_mask, out, gate_w,
+                           gate_b)
         B, T_q, D = x_q.shape
         T_k = T_q if x_kv is None else x_kv.shape[1]
         ydt = {"fp32": torch.float32, "bf16": torch.bfloat16}[y_dtype]
@@ -287,13 +292,14 @@ class MultiHeadAttention:
                 self._ptr(b_qkv, dt), self._ptr(w_o, dt), self._ptr(b_o, dt), B, T_q, T_k,
                 1 if causal else 0, self._ptr(key_padding_mask), self._ptr(out, ydt),
                 workspace.data_ptr(), workspace.numel())
-        if not residual and y_dtype == "fp32" and attn_weights is None:
+        if not residual and y_dtype == "fp32" and attn_weights is None and gate_w is None:
             st = mha_forward(*args, stream)
             _check(st, "mha_forward")
         else:
             opts = mha_forward_options(1 if residual else 0, 1 if y_dtype == "bf16" else 0,
                                        self._ptr(attn_weights, torch.float32),
-                                       1 if average_weights else 0)
+                                       1 if average_weights else 0, self._ptr(gate_w, dt),
+                                       self._ptr(gate_b, dt))
             st = mha_forward_ex(*args, opts, stream)
             _check(st, "mha_forward_ex")
         self._record(stream, x_q.device)

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build", "libmha")
 LIB = os.path.join(PKG, "libmha.so")
 
 SOURCES = ["mha_api.hip", "prep.hip", "gemm16.hip", "attn16.hip", "fp32_path.hip", "decode.hip",
-           "weights.hip"]
+           "weights.hip", "gate.hip"]
 
 # Per-source extra flags. The attention and decode kernels keep their MFMA
 # accumulators in ordinary VGPRs (no AGPR copies around the softmax; the d_k =

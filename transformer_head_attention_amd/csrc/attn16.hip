@@ -96,7 +96,8 @@ __device__ __forceinline__ int swz(int row, int c) {
 // at most 64 keys, so their outputs are averages of few value rows and are
 // the largest of the layer; they are evaluated a second time here from the
 // fp32 Q/K/V the QKV epilogue saved, and their output projection
-// (early_out_kernel) later overwrites those rows of Y. The workgroups doing
+// (early_out_kernel, which also applies the gates of gated attention to
+// them) later overwrites those rows of Y. The workgroups doing
 // this come first in the attention grid (their count rounded up to a
 // multiple of 8, so the attention blocks keep their XCD placement); being
 // short, they leave room to the long causal blocks within microseconds,
@@ -547,14 +548,17 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
     }
   }
 
-  // O = acc / l; head `head` occupies columns [head*DK, (head+1)*DK) of (B, T_q, D).
+  // O = acc / l (times the head's gate under gated attention); head `head`
+// occupies columns [head*DK, (head+1)*DK) of (B, T_q, D).
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
     const float l0 = __shfl(lacc[qi][0], lq & 15), l1 = __shfl(lacc[qi][1], lq & 15);
     const float lt = lq < 16 ? l0 : l1;
-    const float inv = 1.0f / lt;
+    float inv = 1.0f / lt;
     const int row = qw0 + qi * 32 + lq;
     if (row < a.T_q) {
+      // gated attention: the head's output row times its gate
+      if (a.gate) inv *= gate_sigmoid(a.gate[((size_t)b * a.T_q + row) * a.h + head]);
       uint16_t* op = a.o + ((size_t)b * a.T_q + row) * a.D + head * DK;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)

@@ -101,6 +101,13 @@ __device__ __forceinline__ float load_bias_bf16(const uint16_t* b, int i) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// 1 / (1 + e^-x), the gate of gated attention, with the hardware exp2 and
+// reciprocal (each about 1 ulp). e^-x is exp2(-x log2 e): +inf for very
+// negative x (rcp(inf) = 0), 0 for very large x (result 1).
+__device__ __forceinline__ float gate_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
 // Maximum of three / two floats. __builtin_elementwise_maximum (IEEE
 // maximum: a NaN operand gives NaN) lowers to gfx950's v_maximum3_f32, which
 // takes its operands as they are: fmaxf (maxnum) on values the compiler

@@ -254,9 +254,12 @@ attn_f32_kernel(AttnF32Args a) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) o[c] = __builtin_fmaf(accs[w][r][p * 16 + c], f, o[c]);
   }
+  // gated attention: the head's output row times its gate
+  const float gt = a.gate ? gate_sigmoid(a.gate[(size_t)b * a.gate_bstride + (size_t)t * a.h + head])
+                          : 1.0f;
   float* op = a.o + (size_t)b * a.o_bstride + (size_t)t * a.o_ld + head * DK + p * 16;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) op[c] = o[c] / lt;   // all keys masked: 0 / 0 = NaN
+  for (int c = 0; c < 16; ++c) op[c] = o[c] / lt * gt;   // all keys masked: 0 / 0 = NaN
 }
 
 }  // namespace

@@ -590,7 +590,8 @@ constexpr int EO_STAGE = EO_A_BYTES + EO_B_BYTES;
 
 __global__ void __launch_bounds__(EO_WAVES * 64)
 early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __restrict__ WoT,
-                 int N, const uint16_t* __restrict__ bias, OutOptions opt, int R, int T_q) {
+                 int N, const uint16_t* __restrict__ bias, OutOptions opt, int R, int T_q,
+                 const float* __restrict__ gate, int h, int d_k) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[EO_WAVES * 2 * EO_STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -632,7 +633,12 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
   const int mine = nch > wave ? (nch - wave + EO_WAVES - 1) / EO_WAVES : 0;
   if (mine > 0) issue(wave, 0);
   if (mine > 1) issue(wave + EO_WAVES, 1);
+  // gated attention: this lane's row (b, t) of O32; a 64-deep chunk lies in
+  // one head (d_k % 64 == 0), so one gate per lane and chunk
+  const int gm = min(m0 + lq, M - 1), gb = gm / R;
+  const float* grow = gate ? gate + ((size_t)gb * T_q + (gm - gb * R)) * h : nullptr;
   for (int i = 0; i < mine; ++i) {
+    const float gt = grow ? gate_sigmoid(grow[(wave + i * EO_WAVES) * EO_KC / d_k]) : 1.0f;
     if (i + 1 < mine) wait_vmcnt<LPC>();
     else wait_vmcnt<0>();
     const uint8_t* as = wbase + (i & 1) * EO_STAGE;
@@ -651,7 +657,8 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
         bf[j] = *reinterpret_cast<const u32x4*>(bs + row * 128 +
                                                 (((2 * ks + lh) ^ ((row >> 1) & 7)) << 4));
       }
-      const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const float av[8] = {a0[0] * gt, a0[1] * gt, a0[2] * gt, a0[3] * gt,
+                           a1[0] * gt, a1[1] * gt, a1[2] * gt, a1[3] * gt};
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -792,11 +799,12 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
 
 hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
                             const uint16_t* bias, const OutOptions& opt, int R, int T_q,
-                            hipStream_t s) {
+                            const float* gate, int h, int d_k, hipStream_t s) {
   if (N % (32 * EO_TN) != 0 || K % EO_KC != 0 || M < 1) return hipErrorInvalidValue;
+  if (gate && (d_k < EO_KC || d_k % EO_KC != 0 || h * d_k != K)) return hipErrorInvalidValue;
   dim3 grid(N / (32 * EO_TN), (M + 31) / 32);
   hipLaunchKernelGGL(early_out_kernel, grid, dim3(EO_WAVES * 64), 0, s, O32, M, K, WoT, N, bias, opt,
-                     R, T_q);
+                     R, T_q, gate, h, d_k);
   return hipGetLastError();
 }
 

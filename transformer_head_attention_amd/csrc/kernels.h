@@ -29,9 +29,16 @@ struct MaskScan {
   int* kend;
   uint32_t* bits;
 };
-// The transposes j0 and (if non-null) j1 and the mask scan, in one launch.
-hipError_t launch_prep(const TransposeJob& j0, const TransposeJob* j1, const MaskScan& ms,
-                       hipStream_t s);
+// Element-wise transpose of a small (K x N) bf16 matrix, any N: WT[n][k] = W[k][n].
+struct SmallTranspose {
+  const uint16_t* W;   // null: nothing to do
+  uint16_t* WT;
+  int K, N;
+};
+// The transposes j0 and (if non-null) j1, the small transpose and the mask
+// scan, in one launch.
+hipError_t launch_prep(const TransposeJob& j0, const TransposeJob* j1, const SmallTranspose& st,
+                       const MaskScan& ms, hipStream_t s);
 // order[r] = the batch element with the r-th largest kend (ties by index).
 constexpr int kMaskOrderMaxB = 1024;
 hipError_t launch_mask_order(const int* kend, int B, int* order, hipStream_t s);
@@ -70,9 +77,11 @@ hipError_t launch_gemm_out(const uint16_t* A, int M, int K, const uint16_t* Bt, 
 
 // Early causal rows: Y[b*T_q + t] = O32[b*R + t] . W_O + bias [+ resid] for t < R, from
 // fp32 O32 (M = B*R rows x K) and fp16 W_O^T (N x K); N % 32 == 0, K % 64 == 0.
+// gate (nullable): gated attention, head i's columns [i*d_k, (i+1)*d_k) of O32
+// row (b, t) times 1 / (1 + exp(-gate[(b*T_q + t)*h + i])); d_k % 64 == 0.
 hipError_t launch_early_out(const float* O32, int M, int K, const uint16_t* WoT, int N,
                             const uint16_t* bias, const OutOptions& opt, int R, int T_q,
-                            hipStream_t s);
+                            const float* gate, int h, int d_k, hipStream_t s);
 
 // ---- fused attention, fp16 operands, fp32 softmax state ------------------
 struct AttnF16Args {
@@ -85,6 +94,8 @@ struct AttnF16Args {
   const int* kend;     // (B) key extent from the mask; read only with mbits
   const int* order;    // (B) batch elements by key extent, longest first; read only
                        // with mbits; null: natural order
+  const float* gate;   // (B*T_q, h) gate pre-activations g (row b*T_q + t): head i's output
+                       // row t is multiplied by 1 / (1 + exp(-g)); null: no gate
   int B, h, h_kv, T_q, T_k, Tqp, Tkp, D, causal;
   int group_units;     // set by launch_attn_f16 (causal query-block interleave)
 };
@@ -112,11 +123,21 @@ struct AttnF32Args {
   float* o; long o_bstride; int o_ld;
   const uint8_t* mask;                          // (B, mask_ld) nonzero = ignore, or null
   int mask_ld;
+  const float* gate; long gate_bstride;         // gate[b*gate_bstride + t*h + head], or null
   int B, h, rows, T_k, causal;                 // rows = query rows evaluated (t = 0..rows-1)
 };
 hipError_t launch_attn_f32(const AttnF32Args& a, int d_k, hipStream_t s);
 // y[i] += x[i] for i < n (fp32).
 hipError_t launch_add_residual_f32(float* y, const float* x, size_t n, hipStream_t s);
+
+// ---- gated attention ------------------------------------------------------
+// g[m][n] = x[m] . W_G[:, n] + b_G[n] (fp32) for M rows and h gates.
+// bf16: x (M x D), wgT = W_G^T (h x D), bias (h) or null; D % 128 == 0.
+hipError_t launch_gate_bf16(const uint16_t* x, int M, int D, const uint16_t* wgT,
+                            const uint16_t* bias, int h, float* g, hipStream_t s);
+// fp32: x (M x D), wg = W_G (D x h) row-major, bias (h) or null.
+hipError_t launch_gate_f32(const float* x, int M, int D, const float* wg, const float* bias, int h,
+                           float* g, hipStream_t s);
 
 // ---- attention weights (inspection output) --------------------------------
 // A[b][head][t][j] (or the mean over heads) = softmax over keys j of

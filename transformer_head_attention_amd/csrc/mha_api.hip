@@ -56,7 +56,7 @@ int round_up(int x, int a) { return (x + a - 1) / a * a; }
 struct Layout {
   // byte offsets into the workspace
   size_t wqkvT = 0, woT = 0, q = 0, k = 0, vt = 0, o = 0, kend = 0, order = 0, mbits = 0, eqkv = 0,
-         eo = 0;
+         eo = 0, wgT = 0, gate = 0;
   size_t f_q = 0, f_kv = 0, f_o = 0;
   size_t total = 0;
   int Tqp = 0, Tkp = 0, R = 0;
@@ -88,6 +88,8 @@ Layout make_layout(const mha_handle* hd, int B, int T_q, int T_k) {
     L.mbits = take((size_t)B * mha::attn_mask_tiles(T_k) * 8);
     L.eqkv = take((size_t)B * L.R * Nqkv * 4);
     L.eo = take((size_t)B * L.R * D * 4);
+    L.wgT = take((size_t)hd->h * D * 2);
+    L.gate = take((size_t)B * T_q * hd->h * 4);
   } else {
     // One region: self-attention uses it as a single (B*T, N_qkv) buffer;
     // cross-attention as Q (B*T_q, D) followed by [K|V] (B*T_k, 2 Dkv).
@@ -95,6 +97,7 @@ Layout make_layout(const mha_handle* hd, int B, int T_q, int T_k) {
     L.f_q = take((size_t)B * T_q * D * 4 + (size_t)B * T_k * 2 * Dkv * 4);
     L.f_kv = L.f_q + (size_t)B * T_q * D * 4;
     L.f_o = take((size_t)B * T_q * D * 4);
+    L.gate = take((size_t)B * T_q * hd->h * 4);
   }
   L.total = off;
   return L;
@@ -129,6 +132,10 @@ mha_status_t check_forward_args(const mha_handle* hd, const void* x_q, const voi
       (average != 0 && average != 1))
     return MHA_ERR_INVALID_ARG;
   if (weights && !aligned16(weights)) return MHA_ERR_INVALID_ARG;
+  const void* gate_w = opts ? opts->gate_w : nullptr;
+  const void* gate_b = opts ? opts->gate_b : nullptr;
+  if ((gate_b && !gate_w) || (gate_w && !aligned16(gate_w)) || (gate_b && !aligned16(gate_b)))
+    return MHA_ERR_INVALID_ARG;
   if (y_bf16 && hd->dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
   if (weights && (T_k > mha::kWeightsMaxKeys || B > 65535)) return MHA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return MHA_ERR_INVALID_ARG;
@@ -353,8 +360,12 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
   const int y_bf16 = opts ? opts->y_bf16 : 0;
   float* weights = opts ? opts->attn_weights : nullptr;
   const int average = opts ? opts->average_weights : 0;
+  const void* gate_w = opts ? opts->gate_w : nullptr;
+  const void* gate_b = opts ? opts->gate_b : nullptr;
   const Layout L = make_layout(hd, B, T_q, T_k);
   if (workspace_bytes < L.total) return MHA_ERR_WORKSPACE;
+  // gate pre-activations (B*T_q, h), fp32 (gated attention only)
+  float* gpre = gate_w ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.gate) : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream_);
   char* ws = static_cast<char*>(workspace);
@@ -411,12 +422,19 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
 
     // prep
     // both weight transposes and the mask scan in one launch
+    uint16_t* wgT = reinterpret_cast<uint16_t*>(ws + L.wgT);
     const mha::TransposeJob tq{static_cast<const uint16_t*>(w_qkv), wqkvT, D, Nqkv, 0};
     const mha::TransposeJob to{static_cast<const uint16_t*>(w_o), woT, D, D, 1};
+    const mha::SmallTranspose tg{static_cast<const uint16_t*>(gate_w), wgT, D, h};
     const mha::MaskScan ms{key_padding_mask, B, T_k, kend, mbits};
-    MHA_HIP(mha::launch_prep(tq, &to, ms, s));
+    MHA_HIP(mha::launch_prep(tq, &to, tg, ms, s));
     if (ordered) MHA_HIP(mha::launch_mask_order(kend, B, order, s));
     if (!mark(1)) return MHA_ERR_HIP;
+
+    // gated attention: gate pre-activations from the query-side input
+    if (gate_w)
+      MHA_HIP(mha::launch_gate_bf16(xq, B * T_q, D, wgT, static_cast<const uint16_t*>(gate_b), h,
+                                    gpre, s));
 
     // qkv_proj
     mha::QkvEpilogue e{};
@@ -460,6 +478,7 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     a.mbits_ld = mha::attn_mask_tiles(T_k);
     a.kend = key_padding_mask ? kend : nullptr;
     a.order = ordered ? order : nullptr;
+    a.gate = gpre;
     a.B = B;
     a.h = h;
     a.h_kv = h_kv;
@@ -514,7 +533,7 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     // early_rows
     if (causal) {
       MHA_HIP(mha::launch_early_out(eo, B * L.R, D, woT, D, static_cast<const uint16_t*>(b_o), oo,
-                                    L.R, T_q, s));
+                                    L.R, T_q, gpre, h, d_k, s));
     }
     if (!mark(5)) return MHA_ERR_HIP;
   } else {
@@ -551,6 +570,12 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
       f.kv_bstride = (long)T_k * 2 * Dkv;
     }
     f.group = h / h_kv;
+    if (gate_w) {
+      MHA_HIP(mha::launch_gate_f32(xq, B * T_q, D, static_cast<const float*>(gate_w),
+                                   static_cast<const float*>(gate_b), h, gpre, s));
+      f.gate = gpre;
+      f.gate_bstride = (long)T_q * h;
+    }
     if (!mark(2)) return MHA_ERR_HIP;
     f.o = fo;
     f.o_ld = D;

@@ -13,8 +13,9 @@ constexpr int TT = 64;   // transpose tile edge
 
 // One launch: workgroups [0, tiles_t) transpose weights, WT[n][k] = W[k][n]
 // for up to two matrices (the first `tiles0` workgroups take the first), one
-// 64 x 64 tile each; workgroups past them scan the padding mask of one batch
-// element each.
+// 64 x 64 tile each; workgroups [tiles_t, small_end) transpose a small matrix
+// (the gate weights) one element per thread; workgroups past them scan the
+// padding mask of one batch element each.
 //
 // Transpose: global traffic moves 16 bytes per lane both ways: rows of W are
 // read as 8-element chunks, and each output chunk gathers 8 consecutive k of
@@ -26,11 +27,21 @@ constexpr int TT = 64;   // transpose tile edge
 // mask, and its highest clear bit the tile's last unmasked key. kend[b] = 1 +
 // the last unmasked key, 0 if every key is masked.
 __global__ void __launch_bounds__(256)
-prep_kernel(TransposeJob j0, TransposeJob j1, int tiles0, int tiles_t, MaskScan ms) {
+prep_kernel(TransposeJob j0, TransposeJob j1, int tiles0, int tiles_t, SmallTranspose st,
+            int small_end, MaskScan ms) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[TT][TT + 8];
   __shared__ int red[4];
-  if ((int)blockIdx.x >= tiles_t) {
-    const int b = (int)blockIdx.x - tiles_t;
+  if ((int)blockIdx.x >= tiles_t && (int)blockIdx.x < small_end) {
+    // small transpose: one element per thread, the reads along W's rows
+    const long long i = (long long)((int)blockIdx.x - tiles_t) * 256 + threadIdx.x;
+    if (i < (long long)st.K * st.N) {
+      const int k = (int)(i / st.N), n = (int)(i - (long long)k * st.N);
+      st.WT[(size_t)n * st.K + k] = st.W[i];
+    }
+    return;
+  }
+  if ((int)blockIdx.x >= small_end) {
+    const int b = (int)blockIdx.x - small_end;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int T_k = ms.T_k, ntk = (T_k + 63) / 64;
     const uint8_t* mrow = ms.mask + (size_t)b * T_k;
@@ -108,13 +119,16 @@ static int transpose_tiles(const TransposeJob& j) {
   return ((j.N + TT - 1) / TT) * ((j.K + TT - 1) / TT);
 }
 
-hipError_t launch_prep(const TransposeJob& j0, const TransposeJob* j1, const MaskScan& ms,
-                       hipStream_t s) {
+hipError_t launch_prep(const TransposeJob& j0, const TransposeJob* j1, const SmallTranspose& st,
+                       const MaskScan& ms, hipStream_t s) {
   const long long t0 = transpose_tiles(j0), t1 = j1 ? transpose_tiles(*j1) : 0;
+  const long long ns = st.W ? ((long long)st.K * st.N + 255) / 256 : 0;
   const long long nb = ms.mask ? ms.B : 0;
-  if (t0 + t1 < 1 || t0 + t1 + nb > 0x7fffffffLL || (ms.mask && ms.T_k < 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(t0 + t1 + nb)), dim3(256), 0, s, j0,
-                     j1 ? *j1 : j0, (int)t0, (int)(t0 + t1), ms);
+  if (t0 + t1 < 1 || t0 + t1 + ns + nb > 0x7fffffffLL || (ms.mask && ms.T_k < 1) ||
+      (st.W && (st.K < 1 || st.N < 1)))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(t0 + t1 + ns + nb)), dim3(256), 0, s, j0,
+                     j1 ? *j1 : j0, (int)t0, (int)(t0 + t1), st, (int)(t0 + t1 + ns), ms);
   return hipGetLastError();
 }
 
