@@ -106,7 +106,7 @@ __device__ __forceinline__ int swz(int row, int c) {
 // row sit in LDS as fp32 (rows past the extent zeroed, so the key loops have
 // no branches), the scores in registers: two plain passes (maximum, then
 // exponentials and the weighted sum of V), in log2 units.
-constexpr int ER = 16;   // query rows per early-row workgroup
+constexpr int ER = 16;   // query rows per early-row workgroup of 4 waves (4 rows per wave)
 
 // Sum over the 16 lanes of a DPP row (every lane gets the total):
 // quad_perm xor 1, quad_perm xor 2, row_half_mirror, row_mirror.
@@ -118,28 +118,30 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-long long early_blocks(const AttnF32Args& e) {
-  return (long long)((e.rows + ER - 1) / ER) * e.h * e.B;
+__host__ __device__ inline long long early_blocks(const AttnF32Args& e, int er) {
+  return (long long)((e.rows + er - 1) / er) * e.h * e.B;
 }
 
-// blk: (row block, head, batch element) of the early rows; lds: at least
-// 2 * 64 * DK * 4 bytes.
-template <int DK>
+// blk: (row block, head, batch element) of the early rows, NWV waves of 4
+// rows each; lds: at least 2 * 64 * DK * 4 bytes.
+template <int DK, int NWV>
 __device__ __forceinline__ void early_rows_block(const AttnF32Args& a, int blk, uint8_t* lds) {
   constexpr int CPL = DK / 16;   // dimensions per lane
+  constexpr int ERW = NWV * 4;   // query rows per workgroup
+  constexpr int NTW = NWV * 64;
   float (*Ks)[DK] = reinterpret_cast<float (*)[DK]>(lds);
   float (*Vs)[DK] = reinterpret_cast<float (*)[DK]>(lds + 64 * DK * 4);
-  const int nx = (a.rows + ER - 1) / ER;
+  const int nx = (a.rows + ERW - 1) / ERW;
   const int bx = blk % nx, head = (blk / nx) % a.h, b = blk / (nx * a.h);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p = lane & 15;
-  const int t = bx * ER + wave * 4 + (lane >> 4);
+  const int t = bx * ERW + wave * 4 + (lane >> 4);
   const bool valid = t < a.rows;
-  const int kend = a.causal ? min(a.T_k, bx * ER + ER) : a.T_k;   // <= 64 (host-checked)
+  const int kend = a.causal ? min(a.T_k, bx * ERW + ERW) : a.T_k;   // <= 64 (host-checked)
 
   const float* kb = a.k + (size_t)b * a.kv_bstride + (head / a.group) * DK;
   const float* vb = a.v + (size_t)b * a.kv_bstride + (head / a.group) * DK;
-  for (int idx = tid; idx < 64 * (DK / 4); idx += NT) {
+  for (int idx = tid; idx < 64 * (DK / 4); idx += NTW) {
     const int key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
     f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
     if (key < kend) {
@@ -199,50 +201,17 @@ __device__ __forceinline__ void early_rows_block(const AttnF32Args& a, int blk, 
   }
 }
 
-// d_k = 128: the register budget is capped at two waves per SIMD (247 VGPRs,
-// no spill); with two pipeline stages (64 KiB of LDS) two workgroups then
-// share a CU.
-template <int DK, int NQ, int NS, bool HAS_MASK>
-__global__ void __launch_bounds__(NT, (DK == 128 ? 2 : 1))
-attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
-  constexpr int BLOCK_M = NWAVES * 32 * NQ;
-  constexpr int KCH = DK / 8;                       // 16-byte chunks per K row
-  constexpr int K_BYTES = BLOCK_N * DK * 2;
-  constexpr int V_BYTES = DK * BLOCK_N * 2;
-  constexpr int STAGE = K_BYTES + V_BYTES;
-  constexpr int K_LPT = K_BYTES / 16 / NT;          // DMA loads per thread per tile
-  constexpr int V_LPT = V_BYTES / 16 / NT;
-  constexpr int LPT = K_LPT + V_LPT + (HAS_MASK ? 1 : 0);
-  constexpr int KSTEPS = DK / 16;
-  constexpr int DT = DK / 32;
-  static_assert(NS >= 2 && NS <= 4, "pipeline depth");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
-  __shared__ __attribute__((aligned(16))) uint32_t mask_s[NS][2];
-
-  // The first early_slots workgroups evaluate the early causal rows.
-  if ((int)blockIdx.x < early_slots) {
-    static_assert(NS * STAGE >= 2 * 64 * DK * 4, "early-row staging fits the stages");
-    if ((long long)blockIdx.x < (long long)((early.rows + ER - 1) / ER) * early.h * early.B)
-      early_rows_block<DK>(early, (int)blockIdx.x, smem);
-    return;
-  }
-  // wave index in a scalar register: the query rows of the wave, the DMA LDS
-  // bases and the causal tests on them stay scalar
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lq = lane & 31, lh = lane >> 5;
-
-  // Workgroup -> (batch, head, query block). All query blocks of the heads
-  // that share one key/value set run on one XCD and share its L2 copy of K
-  // and V; under the causal mask the longest blocks are dispatched first.
-  // With a padding mask the work of a batch element grows with its key
-  // extent: the units (batch element, key/value set) are taken in `order`
-  // (longest extent first) and dealt round-robin to the 8 XCDs (hardware
-  // block L runs on XCD L % 8), so every XCD gets a like share and starts
-  // with its longest units.
-  const int nqb = a.Tqp / BLOCK_M;
-  const int L = (int)blockIdx.x - early_slots;
-  int b, head, qblk;
+// Workgroup L (after the early-row workgroups) -> (batch, head, query block)
+// for nqb query blocks per (batch, head). All query blocks of the heads that
+// share one key/value set run on one XCD and share its L2 copy of K and V;
+// under the causal mask the longest blocks are dispatched first. With a
+// padding mask the work of a batch element grows with its key extent: the
+// units (batch element, key/value set) are taken in `order` (longest extent
+// first) and dealt round-robin to the 8 XCDs (hardware block L runs on XCD
+// L % 8), so every XCD gets a like share and starts with its longest units.
+template <bool HAS_MASK>
+__device__ __forceinline__ void map_block(const AttnF16Args& a, int L, int nqb, int& b, int& head,
+                                          int& qblk) {
   if (HAS_MASK && a.order != nullptr) {
     const int gh = a.h / a.h_kv, WU = gh * nqb, U = a.B * a.h_kv;
     int us, w;
@@ -279,6 +248,47 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
     head = bh0 - b * a.h;
   }
   if (a.causal) qblk = nqb - 1 - qblk;
+}
+
+// d_k = 128: the register budget is capped at two waves per SIMD (247 VGPRs,
+// no spill); with two pipeline stages (64 KiB of LDS) two workgroups then
+// share a CU.
+template <int DK, int NQ, int NS, bool HAS_MASK>
+__global__ void __launch_bounds__(NT, (DK == 128 ? 2 : 1))
+attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
+  constexpr int BLOCK_M = NWAVES * 32 * NQ;
+  constexpr int KCH = DK / 8;                       // 16-byte chunks per K row
+  constexpr int K_BYTES = BLOCK_N * DK * 2;
+  constexpr int V_BYTES = DK * BLOCK_N * 2;
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int K_LPT = K_BYTES / 16 / NT;          // DMA loads per thread per tile
+  constexpr int V_LPT = V_BYTES / 16 / NT;
+  constexpr int LPT = K_LPT + V_LPT + (HAS_MASK ? 1 : 0);
+  constexpr int KSTEPS = DK / 16;
+  constexpr int DT = DK / 32;
+  static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+  // One LDS array (the tiles' masks at its end): with a second LDS variable
+  // the compiler attaches alias scopes to the accesses and then makes every
+  // LDS read wait for all outstanding global->LDS copies into the array.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE + 32];
+  uint32_t (*mask_s)[2] = reinterpret_cast<uint32_t (*)[2]>(smem + NS * STAGE);
+
+  // The first early_slots workgroups evaluate the early causal rows.
+  if ((int)blockIdx.x < early_slots) {
+    static_assert(NS * STAGE >= 2 * 64 * DK * 4, "early-row staging fits the stages");
+    if ((long long)blockIdx.x < early_blocks(early, ER))
+      early_rows_block<DK, NWAVES>(early, (int)blockIdx.x, smem);
+    return;
+  }
+  // wave index in a scalar register: the query rows of the wave, the DMA LDS
+  // bases and the causal tests on them stay scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, lh = lane >> 5;
+
+  const int nqb = (a.T_q + BLOCK_M - 1) / BLOCK_M;
+  int b, head, qblk;
+  map_block<HAS_MASK>(a, (int)blockIdx.x - early_slots, nqb, b, head, qblk);
   const int bh = b * a.h + head;
   // Key/value set of this query head: consecutive heads share one set, and
   // their workgroups are consecutive in the XCD mappings above, so a set's K
@@ -574,6 +584,7 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   }
 }
 
+
 // Query tiles (of 32 rows) per wave and pipeline depth per head size.
 #ifndef MHA_ATTN_NQ64
 #define MHA_ATTN_NQ64 1
@@ -607,6 +618,9 @@ int attn_mask_tiles(int T_k) { return (T_k + BLOCK_N - 1) / BLOCK_N; }
 hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* early,
                            hipStream_t s) {
   if (a.h_kv < 1 || a.h % a.h_kv != 0) return hipErrorInvalidValue;
+  const int bm = attn_f16_block_m(d_k);
+  // early rows per workgroup: 4 per wave
+  const int er = ER;
   AttnF32Args e{};
   int extra = 0;
   if (early) {
@@ -615,12 +629,13 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
         early->h % early->group != 0)
       return hipErrorInvalidValue;
     e = *early;
-    const long long n = (early_blocks(e) + 7) / 8 * 8;
+    const long long n = (early_blocks(e, er) + 7) / 8 * 8;
     if (n > 0x7fffffffLL) return hipErrorInvalidValue;
     extra = (int)n;
   }
-  const int bm = attn_f16_block_m(d_k);
-  const int total = (a.Tqp / bm) * a.h * a.B;
+  if (a.Tqp % bm != 0 || a.Tkp % bm != 0 || a.Tqp < a.T_q || a.Tkp < a.T_k)
+    return hipErrorInvalidValue;
+  const int total = ((a.T_q + bm - 1) / bm) * a.h * a.B;
   // Causal, unpadded: query blocks of groups of G units are interleaved
   // longest first. G keeps the group's K and V (4 Tkp d_k bytes per key/value
   // set, shared by h / h_kv heads) within MHA_ATTN_GROUP_BYTES, at most 16 and
