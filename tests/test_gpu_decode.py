@@ -63,8 +63,14 @@ def _err(y, ref):
 
 
 def _check_cache(before, after, new_ref, lens, T_new, acc_err=None):
-    """Appended rows: within one bf16 ulp of the oracle (plus, where given,
-    the fp32 accumulation bound of each value); all others unchanged."""
+    """Appended rows: within one bf16 ulp of the oracle plus, where given,
+    (1 + 2^-8) times the fp32 accumulation bound a of each value; all others
+    unchanged.
+
+    The kernel stores bf16(v), v its fp32 value with |v - v_ref| <= a. Round
+    to nearest even moves v by at most half an ulp, 2^-8 |v| <= 2^-8
+    (|v_ref| + a), so |bf16(v) - v_ref| <= 2^-8 |v_ref| + (1 + 2^-8) a; the
+    test allows a full ulp (2^-7 |v_ref|) for the rounding term."""
     b4 = before.view(torch.int16).numpy()
     af = after.view(torch.int16).numpy()
     aft = after.double().numpy()
@@ -78,7 +84,7 @@ def _check_cache(before, after, new_ref, lens, T_new, acc_err=None):
         ref = new_ref[b]
         ulp = np.maximum(np.abs(ref), 2.0 ** -126) * 2.0 ** -7
         if acc_err is not None:
-            ulp = ulp + 2.0 * acc_err[b]
+            ulp = ulp + (1.0 + 2.0 ** -8) * acc_err[b]
         bad = np.abs(got - ref) > ulp
         if bad.any():
             i = np.unravel_index(np.argmax(np.abs(got - ref) - ulp), ref.shape)
