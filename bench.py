@@ -5,7 +5,7 @@ One step = one mha_forward call over one batch of seeded synthetic input
 the fp32 early-row pass), inputs resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline]
+                  [--no-cpu-baseline] [--residual] [--y-dtype fp32|bf16]
 
 Beside the headline rate the line carries:
   roofline      the dominant kernel's algorithmic FLOPs per launch divided by
@@ -16,7 +16,14 @@ Beside the headline rate the line carries:
                 the committed rocprofv3 counter summary, or null when that
                 summary was taken on a different kernel source.
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of
-                the same workload (whole batch elements, about 10 s of work).
+                the same workload (whole batch elements, about 10 s of work),
+                and one full forward of the smallest workload on all threads
+                and on one (full_forward_small).
+
+  python bench.py --oracle-timings [--workload NAME[,NAME...]]
+
+times only the oracle: one full forward of each workload (default all) on
+this host's threads, and the two smallest workloads also single-threaded.
   step_ms       median and minimum of single steps (a further pass, one
                 event pair per step).
   flushed       the same per-step times with 512 MiB written between steps
@@ -174,6 +181,77 @@ def cpu_baseline(w, inp, budget_s: float = 10.0):
                       f"{flops / 1e9:.1f} GFLOP in {spent:.1f} s, fp64 numpy/BLAS"}
 
 
+def _oracle_threads():
+    from threadpoolctl import threadpool_info
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+
+
+def oracle_full_forward(w, inp, single_thread: bool = False, repeats: int = 1):
+    """One full forward of workload w by the fp64 oracle on this host, every
+    batch element and query row (evaluated per batch element and block of
+    query rows, in order), timed (the fastest of `repeats`); optionally with
+    the BLAS restricted to one thread."""
+    from threadpoolctl import threadpool_limits
+    from mha_inputs import as_float64_numpy as f
+    from oracle import mha_oracle
+
+    mask = inp["key_padding_mask"]
+    rows = max(16, (256 << 20) // (w.h * w.T_k * 8))
+    last = [time.perf_counter()]
+
+    def progress(b, t0, t1):
+        now = time.perf_counter()
+        if now - last[0] > 20.0:
+            last[0] = now
+            print(f"[oracle] {w.name}: batch {b}, rows {t1}/{w.T_q}", file=sys.stderr,
+                  flush=True)
+
+    def run():
+        t0 = time.perf_counter()
+        mha_oracle.mha_forward_blocked(
+            f(inp["x_q"]), f(inp["w_qkv"]), f(inp["b_qkv"]), f(inp["w_o"]), f(inp["b_o"]), w.h,
+            x_kv=f(inp["x_kv"]), causal=w.causal,
+            key_padding_mask=None if mask is None else mask.numpy(), n_kv_heads=w.n_g,
+            gate_w=f(inp["gate_w"]), gate_b=f(inp["gate_b"]), rows_per_block=rows,
+            progress=progress)
+        return time.perf_counter() - t0
+
+    if single_thread:
+        with threadpool_limits(1):
+            dt, threads = min(run() for _ in range(repeats)), 1
+    else:
+        dt, threads = min(run() for _ in range(repeats)), _oracle_threads()
+    return {"workload": w.name, "seconds": round(dt, 3),
+            "tflops": round(w.flops() / dt / 1e12, 5), "cores": threads}
+
+
+def oracle_timings(names=None) -> int:
+    """One full forward of each named workload (default every one) by the fp64
+    oracle on this host's cores, and the two smallest also single-threaded
+    (one JSON line)."""
+    from mha_inputs import ALL_WORKLOADS, make_inputs
+    names = list(ALL_WORKLOADS) if names is None else names
+    out = {"kind": "oracle", "host_cpus": len(os.sched_getaffinity(0)), "full_forward": [],
+           "single_thread": []}
+    for name in names:
+        w = ALL_WORKLOADS[name]
+        inp = make_inputs(w, seed=0)
+        r = oracle_full_forward(w, inp, repeats=3 if w.flops() < 1e10 else 1)
+        print(f"[oracle] {name}: {r['seconds']} s on {r['cores']} threads", file=sys.stderr,
+              flush=True)
+        out["full_forward"].append(r)
+    for name in ("self_fp32_d512_h8_b2_t128", "causal_bf16_d512_h8_b16_t1024"):
+        if name not in names:
+            continue
+        w = ALL_WORKLOADS[name]
+        r = oracle_full_forward(w, make_inputs(w, seed=0), single_thread=True,
+                                repeats=3 if w.flops() < 1e10 else 1)
+        print(f"[oracle] {name}: {r['seconds']} s single-threaded", file=sys.stderr, flush=True)
+        out["single_thread"].append(r)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def cpu_baseline_decode(w, inp, budget_s: float = 10.0):
     """fp64 oracle generation step on whole batch elements, one after another
     until about ``budget_s`` seconds of host work."""
@@ -296,7 +374,11 @@ def main() -> int:
     ap.add_argument("--y-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (HBM counter scale)")
+    ap.add_argument("--oracle-timings", action="store_true",
+                    help="run only the fp64 oracle: one full forward per workload on this host")
     args = ap.parse_args()
+    if args.oracle_timings:
+        return oracle_timings(args.workload.split(",") if args.workload else None)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
@@ -402,6 +484,13 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
+        # the smallest workload in full, on all threads and on one
+        from mha_inputs import WORKLOADS as _W
+        w1 = _W["self_fp32_d512_h8_b2_t128"]
+        inp1 = make_inputs(w1, seed=0)
+        line["cpu_baseline"]["full_forward_small"] = [
+            oracle_full_forward(w1, inp1, repeats=3),
+            oracle_full_forward(w1, inp1, True, repeats=3)]
     print(json.dumps(line), flush=True)
     return 0
 
