@@ -59,7 +59,8 @@
  * n_g dividing h, B, T_q, T_k >= 1. fp16 range (bf16 path, which holds W_O
  * and the intermediates in fp16): every W_O entry, every projected Q, K, V
  * value and every attention output must stay below 65504 in magnitude; a
- * larger one becomes +-inf and propagates into y without an error status.
+ * larger one becomes +-inf and propagates into y without an error status
+ * (the fp16_overflow option of mha_forward_ex reports it on the device).
  */
 #ifndef MHA_H
 #define MHA_H
@@ -193,6 +194,16 @@ mha_status_t mha_decode(mha_handle_t handle, const void* x,
  *                  gate_b[i], before the concat and W_O. gate_b without
  *                  gate_w -> MHA_ERR_INVALID_ARG. The attention weights
  *                  output is not gated. Recorded in the "qkv_proj" stage.
+ * fp16_overflow    NULL, or a DEVICE int, 4-byte aligned (else
+ *                  MHA_ERR_INVALID_ARG), that the kernels set to 1 when a
+ *                  value they store in fp16 is not finite: the fp16 copy of
+ *                  W_O, or a projected Q (as stored, times log2(e)/sqrt(d_k)),
+ *                  K or V value of magnitude 65520 or more (past the fp16
+ *                  range) or NaN (a non-finite input). The library never
+ *                  clears it: zero it before the calls it should cover. The
+ *                  attention output needs no check (each of its values is a
+ *                  weighted mean of V values, times a gate in (0, 1)). The
+ *                  fp32 path stores nothing in fp16 and never writes it.
  * Zero-initialise the struct (all fields 0 / NULL are the defaults). */
 typedef struct {
   int residual;
@@ -201,6 +212,7 @@ typedef struct {
   int average_weights;
   const void* gate_w;
   const void* gate_b;
+  int* fp16_overflow;
 } mha_forward_options;
 
 /* mha_forward with options (opts may be NULL: the defaults, all zero, are

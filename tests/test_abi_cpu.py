@@ -204,6 +204,8 @@ def test_forward_options_validation(mha):
         assert call(O(0, 0, fake + 4, 0)) == mha.MHA_ERR_INVALID_ARG  # misaligned weights
         assert call(O(0, 1, None, 0), handle=h32) == mha.MHA_ERR_UNSUPPORTED   # bf16 y, fp32 path
         assert call(O(0, 0, fake, 0), T=5000) == mha.MHA_ERR_UNSUPPORTED        # weights, T_k > 4096
+        assert call(O(0, 0, None, 0, None, None, fake + 2)) == mha.MHA_ERR_INVALID_ARG  # flag
+        assert call(O(0, 0, None, 0, None, None, fake + 2), handle=h32) == mha.MHA_ERR_INVALID_ARG
         assert mha.mha_forward_ex(h, None, None, fake, None, fake, None, 2, 16, 16, 0, None, fake,
                                   fake, ws, O(1, 0, None, 0), None) == mha.MHA_ERR_INVALID_ARG
     finally:

@@ -56,7 +56,8 @@ _lib.mha_forward.restype = _int
 class mha_forward_options(ctypes.Structure):
     _fields_ = [("residual", ctypes.c_int), ("y_bf16", ctypes.c_int),
                 ("attn_weights", ctypes.c_void_p), ("average_weights", ctypes.c_int),
-                ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p)]
+                ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p),
+                ("fp16_overflow", ctypes.c_void_p)]
 
 
 _lib.mha_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
@@ -259,11 +260,13 @@ class MultiHeadAttention:
     def forward(self, x_q, w_qkv, w_o, b_qkv=None, b_o=None, x_kv=None, causal=False,
                 key_padding_mask=None, out=None, workspace=None, stream=None, residual=False,
                 y_dtype="fp32", attn_weights=None, average_weights=False, gate_w=None,
-                gate_b=None):
+                gate_b=None, fp16_overflow=None):
         """Returns y. ``residual`` adds x_q; ``y_dtype`` "bf16" stores y as
         bf16; ``attn_weights`` (a (B, h, T_q, T_k) fp32 tensor, or (B, T_q,
         T_k) with ``average_weights``) receives the softmax weights;
-        ``gate_w`` (D, h) and ``gate_b`` (h,) select gated attention."""
+        ``gate_w`` (D, h) and ``gate_b`` (h,) select gated attention;
+        ``fp16_overflow`` (an int32 device tensor of one element) is set to 1
+        if a value stored in fp16 is not finite (never cleared here)."""
         torch = self._torch
         if x_q.dim() != 3:
             raise ValueError("x_q must be (B, T, D)")
@@ -292,14 +295,18 @@ class MultiHeadAttention:
                 self._ptr(b_qkv, dt), self._ptr(w_o, dt), self._ptr(b_o, dt), B, T_q, T_k,
                 1 if causal else 0, self._ptr(key_padding_mask), self._ptr(out, ydt),
                 workspace.data_ptr(), workspace.numel())
-        if not residual and y_dtype == "fp32" and attn_weights is None and gate_w is None:
+        if fp16_overflow is not None and fp16_overflow.numel() != 1:
+            raise ValueError("fp16_overflow must hold one int32")
+        if (not residual and y_dtype == "fp32" and attn_weights is None and gate_w is None
+                and fp16_overflow is None):
             st = mha_forward(*args, stream)
             _check(st, "mha_forward")
         else:
             opts = mha_forward_options(1 if residual else 0, 1 if y_dtype == "bf16" else 0,
                                        self._ptr(attn_weights, torch.float32),
                                        1 if average_weights else 0, self._ptr(gate_w, dt),
-                                       self._ptr(gate_b, dt))
+                                       self._ptr(gate_b, dt),
+                                       self._ptr(fp16_overflow, torch.int32))
             st = mha_forward_ex(*args, opts, stream)
             _check(st, "mha_forward_ex")
         self._record(stream, x_q.device)

@@ -115,6 +115,17 @@ __device__ __forceinline__ float gate_sigmoid(float x) {
 // input with an extra v_max_f32 x, x. Being ordinary compiler-visible
 // instructions, these also get the wait states a VALU read of an MFMA result
 // needs from the compiler's hazard recogniser.
+// The smallest magnitude that fp16 conversion (round to nearest even) turns
+// into infinity: halfway between 65504 and 2^16.
+constexpr float kF16Overflow = 65520.0f;
+
+// flag (if non-null) := 1 when amax, the largest magnitude a lane converted
+// to fp16, is past the fp16 range or NaN. Lanes that find it write the same
+// value, with a plain vector store.
+__device__ __forceinline__ void flag_f16_overflow(int* flag, float amax) {
+  if (flag && !(amax < kF16Overflow)) *flag = 1;
+}
+
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }

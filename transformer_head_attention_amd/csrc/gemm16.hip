@@ -344,6 +344,8 @@ struct QkEpi {
     }
     // fp16 tile into LDS, one 32-row block at a time (the scheduling fence
     // keeps the compiler from hoisting every block's accumulator reads).
+    // amax: the largest magnitude stored (NaN if a value is NaN).
+    float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = i * 32 + lq;
@@ -354,11 +356,16 @@ struct QkEpi {
           const int c = j * 32 + 8 * rg + 4 * lh;
           float v[4];
           biased(i, j, rg, v);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v[x] *= sc;
+          amax = vmax3(amax, fabsf(v[0]), fabsf(v[1]));
+          amax = vmax3(amax, fabsf(v[2]), fabsf(v[3]));
           *reinterpret_cast<u32x2*>(lds + r * RB + stage_chunk<RB>(r, c >> 3) * 16 + lh * 8) =
-              u32x2{pack_f16x2(v[0] * sc, v[1] * sc), pack_f16x2(v[2] * sc, v[3] * sc)};
+              u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
         }
       __builtin_amdgcn_sched_barrier(0);
     }
+    flag_f16_overflow(e.overflow, amax);
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
     // Write-back. Chunk order: head segment, row, chunk within the segment,
     // so consecutive lanes cover contiguous memory.
@@ -403,6 +410,7 @@ struct VEpi {
     const bool staged = (tw & 15) == 0 && tw + WM <= T && mbase + WM <= M && nbase + WN <= N;
     if (staged) {
       const int hc0 = e.n_base + nbase - v0;
+      float amax = 0.0f;   // the largest magnitude stored (NaN if a value is NaN)
       float bj[TN];   // the wave's bias values, fetched together
       if (e.bias) {
 #pragma unroll
@@ -424,6 +432,8 @@ struct VEpi {
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[i][j][rg * 4 + r] + bias;
+            amax = vmax3(amax, fabsf(v[0]), fabsf(v[1]));
+            amax = vmax3(amax, fabsf(v[2]), fabsf(v[3]));
             if (e.early && tw + r0 < e.early_rows) {
 #pragma unroll
               for (int r = 0; r < 4; ++r)
@@ -436,6 +446,7 @@ struct VEpi {
                 u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
           }
       }
+      flag_f16_overflow(e.overflow, amax);
       __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
       // Write-back: each V^T row segment of WM positions is contiguous.
 #pragma unroll 4
@@ -475,6 +486,7 @@ struct VEpi {
               e.early[((size_t)b * e.early_rows + t) * NQKV + ng] = v[r];
             e.vt[(((size_t)b * e.h_kv + head) * d_k + c) * e.Tpad_kv + vt_pos(t)] =
                 float_to_f16_bits(v[r]);
+            flag_f16_overflow(e.overflow, fabsf(v[r]));
           }
         }
       }

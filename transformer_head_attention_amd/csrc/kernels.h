@@ -19,6 +19,7 @@ struct TransposeJob {
   uint16_t* WT;
   int K, N;
   int to_f16;
+  int* overflow;         // with to_f16: set to 1 if a converted value is not finite, or null
 };
 // Scan of a (B, T_k) padding mask (nonzero = ignore): kend[b] = 1 + last index
 // j with mask[b][j] == 0, or 0 if every key is masked; bits[b][tile] (two
@@ -61,6 +62,7 @@ struct QkvEpilogue {
   float* early;          // (B, early_rows, N_qkv) fp32 copy of rows t < early_rows, or null
   int early_rows;
   float q_scale;         // multiplies the fp16 Q (the fp32 early copy is unscaled)
+  int* overflow;         // set to 1 if a stored fp16 value is not finite, or null
 };
 // A: (M x K) bf16, Bt: (N x K) bf16.
 hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,

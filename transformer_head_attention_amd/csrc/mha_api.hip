@@ -136,6 +136,8 @@ mha_status_t check_forward_args(const mha_handle* hd, const void* x_q, const voi
   const void* gate_b = opts ? opts->gate_b : nullptr;
   if ((gate_b && !gate_w) || (gate_w && !aligned16(gate_w)) || (gate_b && !aligned16(gate_b)))
     return MHA_ERR_INVALID_ARG;
+  const int* ovf = opts ? opts->fp16_overflow : nullptr;
+  if (ovf && (reinterpret_cast<uintptr_t>(ovf) & 3)) return MHA_ERR_INVALID_ARG;
   if (y_bf16 && hd->dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
   if (weights && (T_k > mha::kWeightsMaxKeys || B > 65535)) return MHA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return MHA_ERR_INVALID_ARG;
@@ -362,6 +364,7 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
   const int average = opts ? opts->average_weights : 0;
   const void* gate_w = opts ? opts->gate_w : nullptr;
   const void* gate_b = opts ? opts->gate_b : nullptr;
+  int* const f16_overflow = opts ? opts->fp16_overflow : nullptr;
   const Layout L = make_layout(hd, B, T_q, T_k);
   if (workspace_bytes < L.total) return MHA_ERR_WORKSPACE;
   // gate pre-activations (B*T_q, h), fp32 (gated attention only)
@@ -424,7 +427,7 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     // both weight transposes and the mask scan in one launch
     uint16_t* wgT = reinterpret_cast<uint16_t*>(ws + L.wgT);
     const mha::TransposeJob tq{static_cast<const uint16_t*>(w_qkv), wqkvT, D, Nqkv, 0};
-    const mha::TransposeJob to{static_cast<const uint16_t*>(w_o), woT, D, D, 1};
+    const mha::TransposeJob to{static_cast<const uint16_t*>(w_o), woT, D, D, 1, f16_overflow};
     const mha::SmallTranspose tg{static_cast<const uint16_t*>(gate_w), wgT, D, h};
     const mha::MaskScan ms{key_padding_mask, B, T_k, kend, mbits};
     MHA_HIP(mha::launch_prep(tq, &to, tg, ms, s));
@@ -454,6 +457,7 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     // Q is stored pre-multiplied by log2(e)/sqrt(d_k): the attention kernel
     // then exponentiates scores with exp2 directly.
     e.q_scale = (float)(1.4426950408889634 / std::sqrt((double)d_k));
+    e.overflow = f16_overflow;
     if (!cross) {
       e.T = T_q;
       e.n_base = 0;

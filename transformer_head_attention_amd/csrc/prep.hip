@@ -87,7 +87,11 @@ prep_kernel(TransposeJob j0, TransposeJob j1, int tiles0, int tiles_t, SmallTran
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint16_t v = tile[8 * c + j][nr];
-        if (jb.to_f16) v = float_to_f16_bits(bf16_bits_to_float(v));
+        if (jb.to_f16) {
+          const float f = bf16_bits_to_float(v);
+          v = float_to_f16_bits(f);
+          flag_f16_overflow(jb.overflow, fabsf(f));
+        }
         e[j] = v;
       }
       *reinterpret_cast<u32x4*>(WT + (size_t)n * K + k) =
