@@ -125,6 +125,23 @@ def step_times(torch, stream, step, n: int, flush_bytes: int = 0):
     return sorted(a.elapsed_time(b) for a, b in evs)
 
 
+def warm_up(torch, step, n: int, min_seconds: float):
+    """Untimed warmup: n steps, then further batches of n (at least one step)
+    until min_seconds of wall time have passed, so that the clocks have left
+    their ramp before the timed steps. Returns (steps run, seconds)."""
+    t0 = time.perf_counter()
+    if n <= 0 and min_seconds <= 0:
+        return 0, 0.0
+    batch, done = max(n, 1), 0
+    while True:
+        for _ in range(batch):
+            step()
+        done += batch
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= min_seconds:
+            return done, time.perf_counter() - t0
+
+
 def median(v):
     n = len(v)
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
@@ -294,9 +311,7 @@ def bench_decode(args, name) -> int:
         m.decode(t["x"], t["w_qkv"], t["w_o"], t["k_cache"], t["v_cache"], t["cache_len"],
                  b_qkv=t["b_qkv"], b_o=t["b_o"], out=y, stream=stream.cuda_stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm = warm_up(torch, step, args.warmup, args.warmup_seconds)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -323,6 +338,7 @@ def bench_decode(args, name) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": {"steps": warm[0], "seconds": round(warm[1], 3)},
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -368,6 +384,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="continue the untimed warmup until this much time has passed")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--residual", action="store_true", help="y = x_q + attention output")
@@ -409,11 +427,9 @@ def main() -> int:
                   stream=stream.cuda_stream, residual=args.residual, y_dtype=args.y_dtype,
                   gate_w=t["gate_w"], gate_b=t["gate_b"])
 
-    # Untimed warmup: the first few hundred microseconds of sustained work
-    # run at a different clock than the steady state that follows.
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # Untimed warmup: the first stretch of sustained work runs at a different
+    # clock than the steady state that follows.
+    warm = warm_up(torch, step, args.warmup, args.warmup_seconds)
 
     # Timed region: K steps bracketed by events on the launch stream, with no
     # other events inside (an event record between kernels costs ~5 us).
@@ -452,6 +468,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": {"steps": warm[0], "seconds": round(warm[1], 3)},
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -34,6 +34,7 @@ def check_common(d, steps, warmup):
               "roofline", "cpu_baseline"):
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == steps and d["warmup"] == warmup
+    assert d["warmup_run"]["steps"] >= warmup and d["warmup_run"]["seconds"] >= 0.5
     assert d["value"] > 0 and d["ms_per_step"] > 0
     assert d["higher_is_better"] is True and d["data"] == "synthetic"
     assert "workload" in d["config"]

@@ -23,8 +23,8 @@ SOURCES = ["mha_api.hip", "prep.hip", "gemm16.hip", "attn16.hip", "fp32_path.hip
 
 # Per-source extra flags. The attention and decode kernels keep their MFMA
 # accumulators in ordinary VGPRs (no AGPR copies around the softmax; the d_k =
-# 128 decode kernel drops from 309 to 239 registers); the large GEMM tiles need
-# the AGPR file for their 256 accumulators per lane.
+# 128 decode kernel drops from 309 to 239 registers). The GEMMs are left to
+# the compiler's choice (their 128 accumulators per lane fit the VGPRs).
 _VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 EXTRA = {"attn16.hip": _VGPR_MFMA, "decode.hip": _VGPR_MFMA}
 
