@@ -52,6 +52,7 @@ if ROOT not in sys.path:
 
 METRIC = "MHA fwd TFLOP/s + % bf16 MFMA peak, D=1024 h=16 T=4096 causal, 1 GPU"
 PEAK_MFMA_16BIT_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA, published
+PEAK_MFMA_FP32_TFLOPS = 157.3      # MI355X fp32 matrix, published
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
@@ -460,6 +461,8 @@ def main() -> int:
     dom_ms = stages[dom]
     achieved = stage_flops(w, dom) / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
     traffic = read_traffic(dom, name) if dom in KERNEL_SOURCES else None
+    # the fp32 path runs on the fp32 matrix cores: its own peak
+    peak = PEAK_MFMA_FP32_TFLOPS if w.dtype == "fp32" else PEAK_MFMA_16BIT_TFLOPS
     line = {
         # the headline metric names its workload; other workloads are named in place
         "metric": METRIC if name == HEADLINE else f"MHA fwd TFLOP/s + % bf16 MFMA peak, {name}, 1 GPU",
@@ -479,9 +482,12 @@ def main() -> int:
                    "n_kv_heads": w.n_g, "d_k": w.d_k, "causal": w.causal, "cross": w.cross,
                    "key_padding": w.padding is not None, "gated": w.gate,
                    "gflop_per_step": round(flops / 1e9, 3),
-                   "intermediates": "fp16 Q/K/V/P/O, fp32 accumulate",
+                   "intermediates": ("fp32 Q/K/V/P/O, fp32 accumulate" if w.dtype == "fp32"
+                                     else "fp16 Q/K/V/P/O, fp32 accumulate"),
                    "y": args.y_dtype, "residual": args.residual},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_MFMA_16BIT_TFLOPS, 2),
+        **({"pct_fp32_peak": round(100.0 * tflops / PEAK_MFMA_FP32_TFLOPS, 2)}
+           if w.dtype == "fp32" else {}),
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "step_ms": {"median": round(median(single), 4), "min": round(single[0], 4)},
         "flushed": {"median_ms": round(median(flushed), 4), "min_ms": round(flushed[0], 4),
@@ -492,9 +498,9 @@ def main() -> int:
             "kernel": dom,
             "bound": "mfma",
             "achieved": None if achieved is None else round(achieved, 2),
-            "peak": PEAK_MFMA_16BIT_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": None if achieved is None else round(achieved / PEAK_MFMA_16BIT_TFLOPS, 4),
+            "frac": None if achieved is None else round(achieved / peak, 4),
             "traffic": traffic,
         },
         "cpu_baseline": None,

@@ -70,9 +70,14 @@ def test_bench_cpu_baseline_small_workload():
     d = run_bench("--steps", "3", "--warmup", "1", "--workload", "self_fp32_d512_h8_b2_t128")
     check_common(d, 3, 1)
     assert d["dtype"] == "fp32"
+    # the fp32 path is measured against the fp32 matrix peak
+    assert d["roofline"]["peak"] == 157.3
+    assert abs(d["pct_fp32_peak"] - 100.0 * d["value"] / 157.3) < 0.01
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s"
     assert cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    small = cb["full_forward_small"]
+    assert [r["cores"] for r in small][1] == 1 and all(r["seconds"] > 0 for r in small)
 
 
 def test_bench_decode_line():
