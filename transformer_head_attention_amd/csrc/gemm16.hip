@@ -592,7 +592,8 @@ struct OutEpi {
 // its chunks of O (32 rows, fp32) and of W_O^T (64 columns, fp16) global ->
 // LDS itself (1 KiB contiguous per instruction, two chunks in flight, no
 // workgroup barrier), reads its MFMA fragments from there, and the four
-// partial tiles are summed through LDS in a fixed order.
+// partial tiles are summed through LDS in a fixed order, each wave finishing
+// and storing a quarter of the tile.
 constexpr int EO_WAVES = 4;
 constexpr int EO_TN = 2;                          // 32-column blocks per tile
 constexpr int EO_KC = 64;                         // K per chunk
@@ -693,34 +694,42 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
     }
   }
 
-  // Partial tiles of waves 1..3 through LDS (the staging area is free once
-  // every wave has passed the barrier), summed by wave 0 in wave order.
+  // The four partial tiles through LDS (the staging area is free once every
+  // wave has passed the barrier). Wave w then finishes row group w of the
+  // tile (accumulator elements 4w..4w+3: rows 8w + 4 lh + 0..3), summing the
+  // partials in wave order, so the stores are spread over the four waves.
   __syncthreads();
   f32x16_t(*red)[EO_TN][64] = reinterpret_cast<f32x16_t(*)[EO_TN][64]>(smem);
-  if (wave > 0)
 #pragma unroll
-    for (int j = 0; j < EO_TN; ++j) red[wave - 1][j][lane] = acc[j];
+  for (int j = 0; j < EO_TN; ++j) red[wave][j][lane] = acc[j];
   __syncthreads();
-  if (wave != 0) return;
+  // this lane's four rows of Y (row m of O32 is position t < R of batch bb)
+  size_t yrow[4];
+  bool ok[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = m0 + 8 * wave + 4 * lh + e;
+    ok[e] = m < M;
+    const int bb = m / R, t = m - bb * R;
+    yrow[e] = ((size_t)bb * T_q + t) * N;
+  }
 #pragma unroll
   for (int j = 0; j < EO_TN; ++j) {
+    f32x4_t v = reinterpret_cast<const f32x4_t*>(&red[0][j][lane])[wave];
 #pragma unroll
-    for (int w = 0; w < EO_WAVES - 1; ++w) acc[j] += red[w][j][lane];
+    for (int w = 1; w < EO_WAVES; ++w) v += reinterpret_cast<const f32x4_t*>(&red[w][j][lane])[wave];
     const int n = n0 + 32 * j + lq;
     const float bv = load_bias_bf16(bias, n);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (m < M) {
-        const int bb = m / R, t = m - bb * R;
-        const size_t yi = ((size_t)bb * T_q + t) * N + n;
-        float v = acc[j][r] + bv;
-        if (opt.resid) v += bf16_bits_to_float(opt.resid[yi]);
-        if (opt.y_bf16)
-          static_cast<uint16_t*>(opt.y)[yi] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
-        else
-          static_cast<float*>(opt.y)[yi] = v;
-      }
+    for (int e = 0; e < 4; ++e) {
+      if (!ok[e]) continue;
+      const size_t yi = yrow[e] + n;
+      float y = v[e] + bv;
+      if (opt.resid) y += bf16_bits_to_float(opt.resid[yi]);
+      if (opt.y_bf16)
+        static_cast<uint16_t*>(opt.y)[yi] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
+      else
+        static_cast<float*>(opt.y)[yi] = y;
     }
   }
 }
