@@ -390,8 +390,6 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
     else if (younger == 1) wait_vmcnt<LPT>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();   // every wave's part of tile `it` has landed
-    // The stage read in the previous iteration is free again.
-    if (it + NS - 1 < ntiles) issue(it + NS - 1, (it + NS - 1) % NS);
 
     const uint8_t* Ks = smem + stage * STAGE;
     const uint8_t* Vs = Ks + K_BYTES;
@@ -476,6 +474,11 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       for (int c = 0; c < 4; ++c)
         vf[dt][c] = *reinterpret_cast<const u32x4*>(vrow + swz<8>(row, 2 * c + lh) * 16);
     }
+    // The stage read in the previous iteration is free again (every wave
+    // passed the barrier above). Its refill goes out after this tile's
+    // fragment reads and score MFMAs, which then start sooner after the
+    // barrier.
+    if (it + NS - 1 < ntiles) issue(it + NS - 1, (it + NS - 1) % NS);
     __builtin_amdgcn_sched_barrier(0);
 
     // Phase 2 (per query tile): mask, lazy reference update, P = exp2(S'),
