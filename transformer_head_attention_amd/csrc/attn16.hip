@@ -416,10 +416,15 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       wait_lgkmcnt0();
       __builtin_amdgcn_s_barrier();
     }
+    // The tile's padding-mask bits; every lane reads the same two words, so
+    // whether any key of the tile is masked is a wave-uniform (scalar) test.
     uint64_t bits = 0;
-    if (HAS_MASK)
-      bits = (((uint64_t)mask_s[stage][1] << 32) | mask_s[stage][0]) >> (4 * lh);
-    const bool masked_tile = HAS_MASK || tail;
+    bool mbits = false;
+    if (HAS_MASK) {
+      const uint32_t lo = mask_s[stage][0], hi = mask_s[stage][1];
+      mbits = __builtin_amdgcn_readfirstlane(lo | hi) != 0u;
+      bits = (((uint64_t)hi << 32) | lo) >> (4 * lh);
+    }
 
     // Phase 1: S'^T = K . Q^T - base for every live query tile. All K
     // fragments of the tile are read before the first MFMA (one LDS latency
@@ -489,17 +494,31 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
       const int q_lo = qw0 + qi * 32;
       // Key of accumulator element (kh, r): k0 + kh*32 + 8*(r/4) + 4*lh + r%4.
       const bool diag = a.causal && (k0 + BLOCK_N - 1 > q_lo);
-      if (diag || masked_tile) {
-        const int lim = q_lo + lq - k0 - 4 * lh;   // causal: masked iff rel > lim
-        const int kmax = a.T_k - k0 - 4 * lh;      // past T_k: masked iff rel >= kmax
+      // Element rel (key k0 + 4 lh + rel) lies past the query (causal:
+      // rel > q - k0 - 4 lh) or past T_k (rel >= T_k - k0 - 4 lh) iff
+      // rel > thr; the padding mask adds its own bits where the tile has any.
+      const int kmax = a.T_k - k0 - 4 * lh;
+      const int thr = a.causal ? min(q_lo + lq - k0 - 4 * lh, kmax - 1) : kmax - 1;
+      if constexpr (HAS_MASK) {
+        if (diag || tail || mbits) {
+          // one bit per element: the padding mask's, or above thr
+          const int sh = max(thr + 1, 0);
+          const uint64_t ign = bits | (sh >= 64 ? 0ull : (~0ull << sh));
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rel = kh * 32 + 8 * (r >> 2) + (r & 3);
+              if ((ign >> rel) & 1ull) s[qi][kh][r] = -INFINITY;
+            }
+        }
+      } else if (diag || tail) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rel = kh * 32 + 8 * (r >> 2) + (r & 3);
-            bool ign = (a.causal && rel > lim) || rel >= kmax;
-            if (HAS_MASK) ign = ign || ((bits >> rel) & 1ull);
-            if (ign) s[qi][kh][r] = -INFINITY;
+            if (rel > thr) s[qi][kh][r] = -INFINITY;
           }
       }
 
