@@ -116,6 +116,11 @@ size_t mha_workspace_size(mha_handle_t handle, int B, int T_q, int T_k);
  *                      undefined on entry and exit; must not overlap any
  *                      other argument
  *   stream             hipStream_t or NULL
+ * Sizes: B, T_q, T_k >= 1; B * max(T_q, T_k) < 2^30 and max(T_q, T_k) <
+ * 2^29 - 256 (32-bit row arithmetic); T_k rounded up to a multiple of 256,
+ * times d_k, <= 2^30 (a key/value set's K and V blocks are addressed with
+ * 32-bit byte offsets: about 16M keys at d_k = 64, 8M at d_k = 128). Other
+ * sizes -> MHA_ERR_INVALID_ARG.
  */
 mha_status_t mha_forward(mha_handle_t handle,
                          const void* x_q, const void* x_kv,

@@ -87,6 +87,9 @@ def test_workspace_size(mha):
         assert mha.mha_workspace_size(h, 8, 0, 4096) == 0
         assert mha.mha_workspace_size(None, 8, 4096, 4096) == 0
         assert mha.mha_workspace_size(h, 2, 100, 300) < mha.mha_workspace_size(h, 2, 100, 600)
+        # d_k = 64: a key/value set's K block must stay below 2 GiB (32-bit offsets)
+        assert mha.mha_workspace_size(h, 1, 64, (1 << 24) - 256) > 0
+        assert mha.mha_workspace_size(h, 1, 64, (1 << 24) + 1) == 0
     finally:
         mha.mha_destroy(h)
 

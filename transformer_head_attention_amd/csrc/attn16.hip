@@ -313,23 +313,27 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   // swizzled layout places there. Successive instructions of a tile move 32
   // (K, d_k = 64; V) or 16 (K, d_k = 128) rows on, which leaves the swizzle
   // unchanged, so one byte offset per lane serves all of them: each copy is
-  // a scalar base plus that offset (no per-copy address arithmetic).
+  // a buffer load over the key/value set's K (or V^T) block with that lane
+  // offset and a scalar offset for the tile and the copy (no vector address
+  // arithmetic; the host keeps a block below 2 GiB).
   static_assert((NT / KCH) % 16 == 0 && (NT / 8) % 16 == 0, "swizzle period");
   const int krow0 = tid / KCH, vrow0 = tid / 8;
   const uint32_t koff = (uint32_t)(krow0 * DK + swz<KCH>(krow0, tid % KCH) * 8) * 2u;
   const uint32_t voff = (uint32_t)(vrow0 * a.Tkp + swz<8>(vrow0, tid % 8) * 8) * 2u;
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(Kg, (uint32_t)a.Tkp * DK * 2);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(Vg, (uint32_t)DK * a.Tkp * 2);
   auto issue = [&](int tile, int stage) __attribute__((always_inline)) {
     const int k0 = tile * BLOCK_N;
     uint8_t* kst = smem + stage * STAGE;
     uint8_t* vst = kst + K_BYTES;
-    const uint8_t* kb = reinterpret_cast<const uint8_t*>(Kg + (size_t)k0 * DK);
-    const uint8_t* vb = reinterpret_cast<const uint8_t*>(Vg + k0);
 #pragma unroll
     for (int i = 0; i < K_LPT; ++i)
-      lds_dma16(kb + (size_t)i * (NT / KCH) * DK * 2 + koff, kst + (i * NT + wave * 64) * 16);
+      lds_dma16_buf(rk, koff, (uint32_t)(k0 * DK * 2 + i * (NT / KCH) * DK * 2),
+                    kst + (i * NT + wave * 64) * 16);
 #pragma unroll
     for (int i = 0; i < V_LPT; ++i)
-      lds_dma16(vb + (size_t)i * (NT / 8) * a.Tkp * 2 + voff, vst + (i * NT + wave * 64) * 16);
+      lds_dma16_buf(rv, voff, (uint32_t)(k0 * 2 + i * (NT / 8) * a.Tkp * 2),
+                    vst + (i * NT + wave * 64) * 16);
     if (HAS_MASK) {
       // The tile's two mask dwords; every wave writes the same bytes.
       if (lane < 2)

@@ -54,6 +54,19 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
       (const __attribute__((address_space(1))) void*)gsrc,
       (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
+// Buffer-addressed copies: a resource over a block of global memory (its
+// base in scalar registers) and per-lane and per-copy scalar byte offsets, so
+// a copy needs no vector address arithmetic. Resource word 3 selects raw
+// 32-bit data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base,
+                                           16, voff, soff, 0, 0);
+}
 __device__ __forceinline__ void lds_dma4(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(
       (const __attribute__((address_space(1))) void*)gsrc,

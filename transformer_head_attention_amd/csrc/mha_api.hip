@@ -113,6 +113,9 @@ bool sizes_ok(const mha_handle* hd, int B, int T_q, int T_k) {
   const long long rows = (long long)B * std::max(T_q, T_k);
   if (rows > INT_MAX / 2) return false;
   if ((long long)std::max(T_q, T_k) + 256 > INT_MAX / 4) return false;
+  // the attention kernel addresses one key/value set's K (T_k x d_k) and V^T
+  // (d_k x T_k) blocks, padded to 256 keys, with 32-bit byte offsets
+  if (((long long)T_k + 255) / 256 * 256 * hd->d_k * 2 > INT_MAX) return false;
   (void)D;
   return true;
 }
