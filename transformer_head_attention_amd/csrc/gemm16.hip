@@ -102,7 +102,7 @@ __device__ __forceinline__ void sched_run() {
 // TRANS computes each 32 x 32 tile as (B^T A^T)^T: the MFMA result then holds,
 // per lane, one row m and four consecutive columns n (instead of one column
 // and four consecutive rows).
-template <typename C, typename Tag, bool TRANS, typename Epi>
+template <typename C, typename Tag, bool TRANS, typename Epi, bool BUF>
 __global__ void __launch_bounds__(C::NT, C::OCC)
 gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, int M, int N,
               int K, Epi epi) {
@@ -131,10 +131,31 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   // lands at byte 16*p of the wave's 1 KiB window and fetches the global
   // chunk the swizzled layout places there. Rows past M or N are clamped
   // (their results are never stored).
+  // BUF: the operands are under 2 GiB each, so every copy is a buffer load
+  // with a loop-invariant per-lane byte offset and the slice's scalar offset.
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A, BUF ? (uint32_t)M * K * 2 : 0u);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(Bt, BUF ? (uint32_t)N * K * 2 : 0u);
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     uint8_t* as = smem + stage * C::STAGE;
     uint8_t* bs = as + C::A_BYTES;
     const int k0 = kt * C::BK;
+    if constexpr (BUF) {
+#pragma unroll
+      for (int i = 0; i < C::A_LPT; ++i) {
+        const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
+        const int m = min(m0 + row, M - 1);
+        lds_dma16_buf(ra, (uint32_t)(m * K + c * 8) * 2u, (uint32_t)k0 * 2u,
+                      as + (i * C::NT + wave * 64) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < C::B_LPT; ++i) {
+        const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
+        const int n = min(n0 + row, N - 1);
+        lds_dma16_buf(rb, (uint32_t)(n * K + c * 8) * 2u, (uint32_t)k0 * 2u,
+                      bs + (i * C::NT + wave * 64) * 16);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::A_LPT; ++i) {
       const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
@@ -765,6 +786,10 @@ int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + 
 #ifndef MHA_GEMM_BIG_MIN_TILES
 #define MHA_GEMM_BIG_MIN_TILES 256
 #endif
+// Operands small enough for buffer-addressed copies (32-bit byte offsets).
+bool buf_ok(int M, int N, int K) {
+  return (long long)M * K * 2 <= 0x7fffffffLL && (long long)N * K * 2 <= 0x7fffffffLL;
+}
 bool use_big(int M, int N) {
   return tiles_of(M, N, BigCfg::BM, BigCfg::BN) >= MHA_GEMM_BIG_MIN_TILES;
 }
@@ -778,12 +803,18 @@ template <bool TRANS, typename Epi>
 hipError_t launch_qkv_part(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
                            const Epi& epi, hipStream_t s) {
   if (use_big(M, N)) {
-    hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi>),
+    if (buf_ok(M, N, K)) {
+      hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi, true>),
+                         dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
+                         Bt, M, N, K, epi);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi, false>),
                        dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
                        Bt, M, N, K, epi);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi>),
+  hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi, false>),
                      dim3(tiles_of(M, N, SmallCfg::BM, SmallCfg::BN)), dim3(SmallCfg::NT), 0, s, A,
                      Bt, M, N, K, epi);
   return hipGetLastError();
@@ -838,11 +869,16 @@ hipError_t launch_out_variant(const uint16_t* A, int M, int K, const uint16_t* B
                               const uint16_t* bias, const OutOptions& opt, hipStream_t s) {
   OutEpi<RESID, YBF16> epi{bias, opt.y, opt.resid};
   if (use_big(M, N))
-    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>>),
+    if (buf_ok(M, N, K))
+      hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>, true>),
+                         dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
+                         Bt, M, N, K, epi);
+    else
+    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>, false>),
                        dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
                        Bt, M, N, K, epi);
   else
-    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, true, OutEpi<RESID, YBF16>>),
+    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, true, OutEpi<RESID, YBF16>, false>),
                        dim3(tiles_of(M, N, SmallCfg::BM, SmallCfg::BN)), dim3(SmallCfg::NT), 0,
                        s, A, Bt, M, N, K, epi);
   return hipGetLastError();
