@@ -578,25 +578,53 @@ struct OutEpi {
         }
       }
       __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+      // The block's staged rows, read back together (one LDS latency), then
+      // stored: a block wholly inside Y by buffer stores (its rows as the
+      // resource, one lane offset, the row group as a scalar offset), a block
+      // at the edge of Y element-checked.
+      f32x4_t vv[KO];
 #pragma unroll
       for (int k = 0; k < KO; ++k) {
         const int idx = k * 64 + lane, r = idx / CPR, c = idx % CPR;
-        f32x4_t v = *reinterpret_cast<const f32x4_t*>(lds + r * (CPR * 16) + ((c ^ (r & 15)) << 4));
-        const int m = mbase + i * 32 + r, n = nbase + 4 * c;
-        if (m >= M || n >= N) continue;
-        const size_t yi = (size_t)m * N + n;
+        vv[k] = *reinterpret_cast<const f32x4_t*>(lds + r * (CPR * 16) + ((c ^ (r & 15)) << 4));
         if constexpr (RESID) {
           const u32x2 r2 = rr[k];
-          v[0] += __uint_as_float(r2.x << 16);
-          v[1] += __uint_as_float(r2.x & 0xffff0000u);
-          v[2] += __uint_as_float(r2.y << 16);
-          v[3] += __uint_as_float(r2.y & 0xffff0000u);
+          vv[k][0] += __uint_as_float(r2.x << 16);
+          vv[k][1] += __uint_as_float(r2.x & 0xffff0000u);
+          vv[k][2] += __uint_as_float(r2.y << 16);
+          vv[k][3] += __uint_as_float(r2.y & 0xffff0000u);
         }
-        if constexpr (YBF16)
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Y) + yi) =
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        else
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(Y) + yi) = v;
+      }
+      constexpr int ES = YBF16 ? 2 : 4;   // bytes per element of Y
+      if (mbase + i * 32 + 32 <= M && nbase + WN <= N) {
+        const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(
+            static_cast<uint8_t*>(Y) + ((size_t)(mbase + i * 32) * N + nbase) * ES,
+            (uint32_t)(32 * N * ES));
+        const uint32_t voff = (uint32_t)((lane / CPR) * N + 4 * (lane % CPR)) * ES;
+#pragma unroll
+        for (int k = 0; k < KO; ++k) {
+          const uint32_t soff = (uint32_t)(k * (64 / CPR) * N * ES);
+          if constexpr (YBF16)
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{pack_bf16x2(vv[k][0], vv[k][1]), pack_bf16x2(vv[k][2], vv[k][3])}, ry,
+                voff, soff, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, vv[k]), ry, voff,
+                                                   soff, 0);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < KO; ++k) {
+          const int idx = k * 64 + lane, r = idx / CPR, c = idx % CPR;
+          const int m = mbase + i * 32 + r, n = nbase + 4 * c;
+          if (m >= M || n >= N) continue;
+          const size_t yi = (size_t)m * N + n;
+          if constexpr (YBF16)
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Y) + yi) =
+                u32x2{pack_bf16x2(vv[k][0], vv[k][1]), pack_bf16x2(vv[k][2], vv[k][3])};
+          else
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(Y) + yi) = vv[k];
+        }
       }
       __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // reads done before the next block
       __builtin_amdgcn_sched_barrier(0);
