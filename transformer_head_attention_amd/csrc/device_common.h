@@ -112,8 +112,6 @@ __device__ __forceinline__ float load_bias_bf16(const uint16_t* b, int i) {
   return b ? bf16_bits_to_float(b[i]) : 0.0f;
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
 // 1 / (1 + e^-x), the gate of gated attention, with the hardware exp2 and
 // reciprocal (each about 1 ulp). e^-x is exp2(-x log2 e): +inf for very
 // negative x (rcp(inf) = 0), 0 for very large x (result 1).
