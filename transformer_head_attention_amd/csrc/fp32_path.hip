@@ -2,8 +2,9 @@
 //
 //  * gemm_f32: C = A . B + bias with v_mfma_f32_16x16x4_f32 (full fp32
 //    products and sums); B and bias may be stored as bf16 (converted exactly).
-//    64-deep K slices, the next one loaded into registers under the current
-//    one's MFMAs.
+//    64- or 128-deep K slices, the next one loaded into registers under the
+//    current one's MFMAs; 32 x 32 tiles when 64 x 64 ones would not fill the
+//    CUs.
 //    Used for X . W_QKV and O . W_O (itwiki "멀티 헤드 어텐션",
 //    텐서 모양으로 본 계산, 투영 and 출력 투영 rows).
 //  * attn_f32: softmax(q . k / sqrt(d_k) + M) v row by row in fp32
@@ -21,73 +22,80 @@ namespace mha {
 
 namespace {
 
-constexpr int FBM = 64, FBN = 64, FBK = 64;
-
-// 64 x 64 tile per workgroup (4 waves of 32 x 32), K in 64-deep slices; the
-// next slice is loaded into registers while the current one is multiplied
-// from LDS, so each slice costs one global latency at most once.
-template <bool B_BF16>
+// TBM x TBN tile per workgroup (4 waves, 2 x 2, of TBM/2 x TBN/2), K in
+// TBK-deep slices; the next slice is loaded into registers while the current
+// one is multiplied from LDS, so each slice costs one global latency at most
+// once. Small problems take 32 x 32 tiles (more workgroups) and deep K takes
+// 128-deep slices (half the latency-bound steps).
+template <bool B_BF16, int TBM, int TBN, int TBK>
 __global__ void __launch_bounds__(256)
 gemm_f32_kernel(const float* __restrict__ A, int lda, int M, int K, const void* __restrict__ Bv,
                 int ldb, int N, const void* __restrict__ biasv, float* __restrict__ C, int ldc,
                 int rows_in, int rows_out) {
-  __shared__ float As[FBM][FBK + 1];
-  __shared__ float Bs[FBK][FBN + 4];
+  static_assert(TBM % 32 == 0 && TBN % 32 == 0 && TBK % 64 == 0, "tile shape");
+  constexpr int WI = TBM / 32, WJ = TBN / 32;     // 16 x 16 blocks per wave
+  constexpr int ACH = TBK / 4, BCH = TBN / 4, BCH8 = TBN / 8;
+  constexpr int A_V4 = TBM * TBK / 4 / 256;       // float4 loads per thread
+  constexpr int B_V4 = TBK * TBN / 4 / 256;
+  constexpr int B_H8 = TBK * TBN / 8 / 256;       // 8 x bf16 loads per thread
+  static_assert(A_V4 * 1024 == TBM * TBK && B_H8 * 2048 == TBK * TBN, "loads per thread");
+  __shared__ float As[TBM][TBK + 1];
+  __shared__ float Bs[TBK][TBN + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * FBM, n0 = blockIdx.x * FBN;
+  const int m0 = blockIdx.y * TBM, n0 = blockIdx.x * TBN;
 
-  f32x4_t acc[2][2];
+  f32x4_t acc[WI][WJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // A slice: 64 rows x 64 k (4 float4 per thread); B slice: 64 k x 64 n, as
-  // 4 float4 (fp32) or 2 x 8 bf16 per thread. Rows past M are clamped (never
-  // stored); N is a multiple of 64 here.
-  f32x4_t ra[4], rb[4];
-  u32x4 rbh[2];
+  // A slice: TBM rows x TBK k; B slice: TBK k x TBN n, as float4 (fp32) or
+  // 8 x bf16 per load. Rows past M are clamped (never stored); N is a
+  // multiple of TBN here.
+  f32x4_t ra[A_V4], rb[B_BF16 ? 1 : B_V4];
+  u32x4 rbh[B_BF16 ? B_H8 : 1];
   auto load = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = i * 256 + tid, row = p >> 4, c = (p & 15) * 4;
+    for (int i = 0; i < A_V4; ++i) {
+      const int p = i * 256 + tid, row = p / ACH, c = (p % ACH) * 4;
       ra[i] = *reinterpret_cast<const f32x4_t*>(A + (size_t)min(m0 + row, M - 1) * lda + k0 + c);
     }
-    if (!B_BF16) {
+    if constexpr (!B_BF16) {
       const float* Bf = static_cast<const float*>(Bv);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = i * 256 + tid, row = p >> 4, c = (p & 15) * 4;
+      for (int i = 0; i < B_V4; ++i) {
+        const int p = i * 256 + tid, row = p / BCH, c = (p % BCH) * 4;
         rb[i] = *reinterpret_cast<const f32x4_t*>(Bf + (size_t)(k0 + row) * ldb + n0 + c);
       }
     } else {
       const uint16_t* Bb = static_cast<const uint16_t*>(Bv);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int p = i * 256 + tid, row = p >> 3, c = (p & 7) * 8;
+      for (int i = 0; i < B_H8; ++i) {
+        const int p = i * 256 + tid, row = p / BCH8, c = (p % BCH8) * 8;
         rbh[i] = *reinterpret_cast<const u32x4*>(Bb + (size_t)(k0 + row) * ldb + n0 + c);
       }
     }
   };
   auto stash = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = i * 256 + tid, row = p >> 4, c = (p & 15) * 4;
+    for (int i = 0; i < A_V4; ++i) {
+      const int p = i * 256 + tid, row = p / ACH, c = (p % ACH) * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) As[row][c + e] = ra[i][e];
     }
-    if (!B_BF16) {
+    if constexpr (!B_BF16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = i * 256 + tid, row = p >> 4, c = (p & 15) * 4;
+      for (int i = 0; i < B_V4; ++i) {
+        const int p = i * 256 + tid, row = p / BCH, c = (p % BCH) * 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) Bs[row][c + e] = rb[i][e];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int p = i * 256 + tid, row = p >> 3, c = (p & 7) * 8;
+      for (int i = 0; i < B_H8; ++i) {
+        const int p = i * 256 + tid, row = p / BCH8, c = (p % BCH8) * 8;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           Bs[row][c + 2 * e] = __uint_as_float(rbh[i][e] << 16);
@@ -98,28 +106,30 @@ gemm_f32_kernel(const float* __restrict__ A, int lda, int M, int K, const void* 
   };
 
   load(0);
-  for (int k0 = 0; k0 < K; k0 += FBK) {
+  for (int k0 = 0; k0 < K; k0 += TBK) {
     stash();
     __syncthreads();
-    if (k0 + FBK < K) load(k0 + FBK);
+    if (k0 + TBK < K) load(k0 + TBK);
 #pragma unroll
-    for (int kk = 0; kk < FBK / 4; ++kk) {
-      float av[2], bv[2];
+    for (int kk = 0; kk < TBK / 4; ++kk) {
+      float av[WI], bv[WJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = As[wm * 32 + i * 16 + (lane & 15)][kk * 4 + (lane >> 4)];
+      for (int i = 0; i < WI; ++i)
+        av[i] = As[wm * (TBM / 2) + i * 16 + (lane & 15)][kk * 4 + (lane >> 4)];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bv[j] = Bs[kk * 4 + (lane >> 4)][wn * 32 + j * 16 + (lane & 15)];
+      for (int j = 0; j < WJ; ++j)
+        bv[j] = Bs[kk * 4 + (lane >> 4)][wn * (TBN / 2) + j * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x4f32(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < WJ; ++j) acc[i][j] = mfma16x16x4f32(av[i], bv[j], acc[i][j]);
     }
     __syncthreads();
   }
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 32 + j * 16 + (lane & 15);
+  for (int j = 0; j < WJ; ++j) {
+    const int n = n0 + wn * (TBN / 2) + j * 16 + (lane & 15);
     if (n >= N) continue;
     float bias = 0.0f;
     if (biasv) {
@@ -127,10 +137,10 @@ gemm_f32_kernel(const float* __restrict__ A, int lda, int M, int K, const void* 
                     : static_cast<const float*>(biasv)[n];
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + r;
+        const int m = m0 + wm * (TBM / 2) + i * 16 + 4 * (lane >> 4) + r;
         if (m < M) {
           const int g = m / rows_in;
           const size_t out_row = (size_t)g * rows_out + (m - g * rows_in);
@@ -264,17 +274,40 @@ attn_f32_kernel(AttnF32Args a) {
 
 }  // namespace
 
+namespace {
+template <int TBM, int TBN, int TBK>
+void launch_gemm_f32_tiles(const float* A, int lda, int M, int K, const void* B, int ldb, int N,
+                           bool b_bf16, const void* bias, float* C, int ldc, int rows_in,
+                           int rows_out, hipStream_t s) {
+  dim3 grid(N / TBN, (M + TBM - 1) / TBM);
+  if (b_bf16)
+    hipLaunchKernelGGL((gemm_f32_kernel<true, TBM, TBN, TBK>), grid, dim3(256), 0, s, A, lda, M, K,
+                       B, ldb, N, bias, C, ldc, rows_in, rows_out);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<false, TBM, TBN, TBK>), grid, dim3(256), 0, s, A, lda, M,
+                       K, B, ldb, N, bias, C, ldc, rows_in, rows_out);
+}
+}  // namespace
+
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const void* B, int ldb, int N,
                            bool b_bf16, const void* bias, float* C, int ldc, int rows_in,
                            int rows_out, hipStream_t s) {
-  if (K % FBK != 0 || N % FBN != 0 || M < 1) return hipErrorInvalidValue;
-  dim3 grid((N + FBN - 1) / FBN, (M + FBM - 1) / FBM);
-  if (b_bf16)
-    hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, dim3(256), 0, s, A, lda, M, K, B, ldb, N, bias,
-                       C, ldc, rows_in, rows_out);
+  if (K % 64 != 0 || N % 64 != 0 || M < 1) return hipErrorInvalidValue;
+  // 64 x 64 tiles once they fill the 256 CUs, else 32 x 32 (four times the
+  // workgroups); 128-deep K slices when K allows.
+  const bool big = (long long)(N / 64) * ((M + 63) / 64) >= 256, deep = K % 128 == 0;
+  if (big && deep)
+    launch_gemm_f32_tiles<64, 64, 128>(A, lda, M, K, B, ldb, N, b_bf16, bias, C, ldc, rows_in,
+                                       rows_out, s);
+  else if (big)
+    launch_gemm_f32_tiles<64, 64, 64>(A, lda, M, K, B, ldb, N, b_bf16, bias, C, ldc, rows_in,
+                                      rows_out, s);
+  else if (deep)
+    launch_gemm_f32_tiles<32, 32, 128>(A, lda, M, K, B, ldb, N, b_bf16, bias, C, ldc, rows_in,
+                                       rows_out, s);
   else
-    hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, dim3(256), 0, s, A, lda, M, K, B, ldb, N,
-                       bias, C, ldc, rows_in, rows_out);
+    launch_gemm_f32_tiles<32, 32, 64>(A, lda, M, K, B, ldb, N, b_bf16, bias, C, ldc, rows_in,
+                                      rows_out, s);
   return hipGetLastError();
 }
 
