@@ -192,20 +192,38 @@ attn_f32_kernel(AttnF32Args a) {
   const float* vb = a.v + (size_t)b * a.kv_bstride + (head / a.group) * DK;
   const uint8_t* mb = a.mask ? a.mask + (size_t)b * a.mask_ld : nullptr;
 
-  for (int j0 = 0; j0 < kend; j0 += KC) {
-    __syncthreads();
-    for (int idx = tid; idx < KC * DK / 4; idx += ATTN32_NT) {
-      const int key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4, j = j0 + key;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+  // Chunk loads go to registers first: the next chunk's are in flight while
+  // the current one is used from LDS.
+  constexpr int LD = KC * DK / 4 / ATTN32_NT;   // float4 of K (and of V) per thread
+  static_assert(LD * ATTN32_NT * 4 == KC * DK, "chunk / thread mismatch");
+  float4 kr[LD], vr[LD];
+  uint8_t mr = 0;
+  auto load_chunk = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < LD; ++it) {
+      const int idx = it * ATTN32_NT + tid, key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
+      const int j = j0 + key;
+      kr[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vr[it] = kr[it];
       if (j < a.T_k) {
-        kv = *reinterpret_cast<const float4*>(kb + (size_t)j * a.kv_ld + c4);
-        vv = *reinterpret_cast<const float4*>(vb + (size_t)j * a.kv_ld + c4);
+        kr[it] = *reinterpret_cast<const float4*>(kb + (size_t)j * a.kv_ld + c4);
+        vr[it] = *reinterpret_cast<const float4*>(vb + (size_t)j * a.kv_ld + c4);
       }
-      *reinterpret_cast<float4*>(&Ks[key][c4]) = kv;
-      *reinterpret_cast<float4*>(&Vs[key][c4]) = vv;
     }
-    if (tid < KC) Ms[tid] = (mb && j0 + tid < a.T_k) ? mb[j0 + tid] : 0;
+    if (tid < KC) mr = (mb && j0 + tid < a.T_k) ? mb[j0 + tid] : 0;
+  };
+  if (kend > 0) load_chunk(0);
+  for (int j0 = 0; j0 < kend; j0 += KC) {
+    __syncthreads();   // every wave is done with the previous chunk
+#pragma unroll
+    for (int it = 0; it < LD; ++it) {
+      const int idx = it * ATTN32_NT + tid, key = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
+      *reinterpret_cast<float4*>(&Ks[key][c4]) = kr[it];
+      *reinterpret_cast<float4*>(&Vs[key][c4]) = vr[it];
+    }
+    if (tid < KC) Ms[tid] = mr;
     __syncthreads();
+    if (j0 + KC < kend) load_chunk(j0 + KC);
 
     float s[KW];
     float cmax = -INFINITY;
