@@ -67,6 +67,35 @@ __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base,
                                            16, voff, soff, 0, 0);
 }
+// Transposing LDS read of 16-bit values (gfx950). In each group of 16 lanes,
+// lane 4 e + q names 8 bytes holding row e, columns 4 q .. 4 q + 3 of a 4 x 16
+// block; lane j of the group receives column j, rows 0..3 (row 0 in the low
+// 16 bits). Written as assembly: with the builtin form the compiler waits for
+// every global->LDS copy in flight before the read (it does not tell the
+// copies' targets from the read's address), which would serialise a copy
+// pipeline. The caller guarantees the bytes read are not being copied into,
+// and waits for the result with lds_tr_wait before using it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// Waits for every LDS read in flight and makes the values in v and w depend
+// on it, so nothing reading them is scheduled before the wait (and the
+// compiler, which cannot see the wait, adds none of its own for them).
+template <int N, int M>
+__device__ __forceinline__ void lds_tr_wait(u32x4 (&v)[N], u32x4 (&w)[M]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]));
+#pragma unroll
+  for (int i = 1; i < N; ++i) asm volatile("" : "+v"(v[i]));
+#pragma unroll
+  for (int i = 0; i < M; ++i) asm volatile("" : "+v"(w[i]));
+}
 __device__ __forceinline__ void lds_dma4(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(
       (const __attribute__((address_space(1))) void*)gsrc,

@@ -9,10 +9,11 @@
 //  * Output projection (same table, 출력 투영 row): Y = O . W_O + b_O with
 //    fp16 operands, fp32 accumulation and an fp32 result.
 //
-// Both operands are K-contiguous (A row-major M x K, B given transposed as
-// N x K). Tiles are staged through LDS, double-buffered with a register
-// prefetch of the next K slice; each wave owns a WM x WN sub-tile computed
-// with v_mfma_f32_32x32x16.
+// A is row-major M x K. The QKV projection reads W_QKV as it is given (K x N
+// row-major, through transposing LDS reads); the output projection reads
+// W_O^T (N x K, converted to fp16 by the preparation kernel). Tiles are staged
+// through LDS by asynchronous global->LDS copies, two K slices in flight;
+// each wave owns a WM x WN sub-tile computed with v_mfma_f32_32x32x16.
 #include <utility>
 
 #include <type_traits>
@@ -99,13 +100,27 @@ __device__ __forceinline__ void sched_run() {
   sched_run<SLOTS, NR, NV>(std::make_integer_sequence<int, SLOTS>{});
 }
 
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order.
+template <typename F, int... S>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, S...>) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 // TRANS computes each 32 x 32 tile as (B^T A^T)^T: the MFMA result then holds,
 // per lane, one row m and four consecutive columns n (instead of one column
 // and four consecutive rows).
-template <typename C, typename Tag, bool TRANS, typename Epi, bool BUF>
+// BROW: the second operand is given row-major, B (K x N, row stride ldb), as
+// the projection weights are, instead of N x K: its K slices are copied as
+// BK rows of BN columns and the MFMA fragments (8 consecutive k of one
+// column per lane) are read with the transposing LDS read.
+template <typename C, typename Tag, bool TRANS, typename Epi, bool BUF, bool BROW>
 __global__ void __launch_bounds__(C::NT, C::OCC)
 gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, int M, int N,
-              int K, Epi epi) {
+              int K, int ldb, Epi epi) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NS * C::STAGE];
   // wave index in a scalar register: the DMA LDS bases below stay scalar
   const int tid = threadIdx.x, lane = tid & 63;
@@ -134,7 +149,12 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   // BUF: the operands are under 2 GiB each, so every copy is a buffer load
   // with a loop-invariant per-lane byte offset and the slice's scalar offset.
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A, BUF ? (uint32_t)M * K * 2 : 0u);
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(Bt, BUF ? (uint32_t)N * K * 2 : 0u);
+  const __amdgpu_buffer_rsrc_t rb =
+      buffer_rsrc(Bt, BUF ? (uint32_t)(BROW ? K * ldb : N * K) * 2 : 0u);
+  // BROW stage layout: BK rows of BCH 16-byte chunks; chunk c of row r sits
+  // at c ^ 4 (r & 3), so the four rows one transposing read takes land on
+  // four different 64-byte bank groups.
+  constexpr int BCH = C::BN / 8;
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     uint8_t* as = smem + stage * C::STAGE;
     uint8_t* bs = as + C::A_BYTES;
@@ -149,10 +169,17 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
       }
 #pragma unroll
       for (int i = 0; i < C::B_LPT; ++i) {
-        const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
-        const int n = min(n0 + row, N - 1);
-        lds_dma16_buf(rb, (uint32_t)(n * K + c * 8) * 2u, (uint32_t)k0 * 2u,
-                      bs + (i * C::NT + wave * 64) * 16);
+        if constexpr (BROW) {
+          const int p = i * C::NT + tid, r = p / BCH, c = (p % BCH) ^ ((r & 3) << 2);
+          const int n = min(n0 + c * 8, N - 8);
+          lds_dma16_buf(rb, (uint32_t)(r * ldb + n) * 2u, (uint32_t)k0 * (uint32_t)ldb * 2u,
+                        bs + (i * C::NT + wave * 64) * 16);
+        } else {
+          const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
+          const int n = min(n0 + row, N - 1);
+          lds_dma16_buf(rb, (uint32_t)(n * K + c * 8) * 2u, (uint32_t)k0 * 2u,
+                        bs + (i * C::NT + wave * 64) * 16);
+        }
       }
       return;
     }
@@ -165,10 +192,16 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
     }
 #pragma unroll
     for (int i = 0; i < C::B_LPT; ++i) {
-      const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
-      const int n = min(n0 + row, N - 1);
-      lds_dma16(Bt + (size_t)n * K + k0 + c * 8,
-                bs + (i * C::NT + wave * 64) * 16);
+      if constexpr (BROW) {
+        const int p = i * C::NT + tid, r = p / BCH, c = (p % BCH) ^ ((r & 3) << 2);
+        const int n = min(n0 + c * 8, N - 8);
+        lds_dma16(Bt + (size_t)(k0 + r) * ldb + n, bs + (i * C::NT + wave * 64) * 16);
+      } else {
+        const int p = i * C::NT + tid, row = p / C::CH, c = swz<C::CH>(row, p % C::CH);
+        const int n = min(n0 + row, N - 1);
+        lds_dma16(Bt + (size_t)n * K + k0 + c * 8,
+                  bs + (i * C::NT + wave * 64) * 16);
+      }
     }
   };
 
@@ -183,20 +216,65 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   const int nk = K / C::BK;
   const int arow0 = wm * C::WM + (lane & 31), brow0 = wn * C::WN + (lane & 31);
   const int lh = lane >> 5;
-  // Operand fragments of one 16-deep k-step, read from a stage.
-  auto frags = [&](const uint8_t* as, int ks, u32x4 (&fa)[C::TM], u32x4 (&fb)[C::TN])
+  // BROW fragment reads: lane 16 g + 4 e + q of a transposing read names row
+  // 16 ks + 8 (g / 2) + 4 h + e (h = 0, 1: the two reads of a fragment) and
+  // columns 32 j + 16 (g % 2) + 4 q .. +3 of the wave's tile; lane l then
+  // holds column l % 32 at k = 16 ks + 8 (l / 32) + 4 h + 0..3, the same k as
+  // the A fragment's 16-byte chunk. Row 16 ks + ... has (row & 3) = e.
+  int trb[C::TN];
+  if constexpr (BROW) {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      trb[j] = (8 * (g >> 1) + e) * BCH * 16 +
+               ((((wn * C::WN + 32 * j) >> 3) ^ (e << 2)) + 2 * (g & 1) + (q >> 1)) * 16 +
+               (q & 1) * 8;
+  }
+  // Operand fragments of one 16-deep k-step, read from a stage (the step is a
+  // compile-time constant: the transposing reads take their offsets as
+  // immediates).
+  auto frags_a = [&](const uint8_t* as, auto ksc, u32x4 (&fa)[C::TM])
       __attribute__((always_inline)) {
-    const uint8_t* bs = as + C::A_BYTES;
+    constexpr int ks = decltype(ksc)::value;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
       const int row = arow0 + i * 32;
       fa[i] = *reinterpret_cast<const u32x4*>(as + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
     }
+  };
+  auto frags_b = [&](const uint8_t* as, auto ksc, u32x4 (&fb)[C::TN])
+      __attribute__((always_inline)) {
+    constexpr int ks = decltype(ksc)::value;
+    const uint8_t* bs = as + C::A_BYTES;
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
-      const int row = brow0 + j * 32;
-      fb[j] = *reinterpret_cast<const u32x4*>(bs + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
+      if constexpr (BROW) {
+        const uint32_t ad = lds_addr(as) + trb[j];
+        const u32x2 lo = lds_read_tr16<C::A_BYTES + 16 * ks * BCH * 16>(ad);
+        const u32x2 hi = lds_read_tr16<C::A_BYTES + (16 * ks + 4) * BCH * 16>(ad);
+        fb[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        const int row = brow0 + j * 32;
+        fb[j] = *reinterpret_cast<const u32x4*>(bs + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
+      }
     }
+  };
+  auto frags = [&](const uint8_t* as, auto ksc, u32x4 (&fa)[C::TM], u32x4 (&fb)[C::TN])
+      __attribute__((always_inline)) {
+    frags_a(as, ksc, fa);
+    frags_b(as, ksc, fb);
+  };
+  auto frag_a_at = [&](const uint8_t* as, auto ksc, int i) __attribute__((always_inline)) {
+    constexpr int ks = decltype(ksc)::value;
+    const int row = arow0 + i * 32;
+    return *reinterpret_cast<const u32x4*>(as + (row * C::CH + swz<C::CH>(row, 2 * ks + lh)) * 16);
+  };
+  auto frag_b_tr_at = [&](const uint8_t* as, auto ksc, int j) __attribute__((always_inline)) {
+    constexpr int ks = decltype(ksc)::value;
+    const uint32_t ad = lds_addr(as) + trb[j];
+    const u32x2 lo = lds_read_tr16<C::A_BYTES + 16 * ks * BCH * 16>(ad);
+    const u32x2 hi = lds_read_tr16<C::A_BYTES + (16 * ks + 4) * BCH * 16>(ad);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
   auto mfma_one = [&](int idx, const u32x4 (&fa)[C::TM], const u32x4 (&fb)[C::TN])
       __attribute__((always_inline)) {
@@ -219,7 +297,8 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   wait_vmcnt<(C::NS - 1) * C::LPT>();
   __builtin_amdgcn_s_barrier();
 
-  constexpr int KS = C::BK / 16, NR = C::TM + C::TN, NMF = C::TM * C::TN;
+  // (NR counts the reads the scheduler sees: not the assembly ones)
+  constexpr int KS = C::BK / 16, NR = C::TM + (BROW ? 0 : C::TN), NMF = C::TM * C::TN;
 #ifndef MHA_GEMM_PRE
 #define MHA_GEMM_PRE 2
 #endif
@@ -229,22 +308,57 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   constexpr int LB = (KS - 1) & 1;   // fragment buffer of the last k-step
   u32x4 a[2][C::TM], b[2][C::TN];
   // All k-steps of slice kt but the last, and the first PRE MFMAs of the last.
+  // BROW: each k-step first waits for its fragments (read during the
+  // previous k-step), then issues the next k-step's transposing reads ahead of
+  // everything else (the scheduler does not count them as LDS reads and would
+  // otherwise leave them to the end of the step), then its A reads spread
+  // over its MFMAs.
   auto slice_head = [&](int kt) __attribute__((always_inline)) {
     const uint8_t* as = smem + (kt % C::NS) * C::STAGE;
+    if constexpr (BROW) {
+      static_for<KS - 1>([&](auto ksc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ksc)::value, cur = ks & 1, nxt = cur ^ 1;
+        lds_tr_wait(b[cur], a[cur]);
+        // MFMA q, then read group q of the next k-step: the TN transposed B
+        // fragments first (two reads each), then the TM A fragments; the
+        // order is fixed with scheduling barriers.
+        static_for<NMF>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          mfma_one(q, a[cur], b[cur]);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (q < C::TN) {
+            b[nxt][q] = frag_b_tr_at(as, std::integral_constant<int, ks + 1>{}, q);
+          } else if constexpr (q < C::TN + C::TM) {
+            a[nxt][q - C::TN] = frag_a_at(as, std::integral_constant<int, ks + 1>{}, q - C::TN);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        static_for<(C::TN + C::TM > NMF ? C::TN + C::TM - NMF : 0)>([&](auto rc)
+            __attribute__((always_inline)) {
+          constexpr int r = decltype(rc)::value + NMF;
+          if constexpr (r < C::TN) b[nxt][r] = frag_b_tr_at(as, std::integral_constant<int, ks + 1>{}, r);
+          else a[nxt][r - C::TN] = frag_a_at(as, std::integral_constant<int, ks + 1>{}, r - C::TN);
+        });
+      });
+      lds_tr_wait(b[LB], a[LB]);
 #pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-      frags(as, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
+      for (int q = 0; q < PRE; ++q) mfma_one(q, a[LB], b[LB]);
+    } else {
+      static_for<KS - 1>([&](auto ksc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ksc)::value;
+        frags(as, std::integral_constant<int, ks + 1>{}, a[(ks + 1) & 1], b[(ks + 1) & 1]);
 #pragma unroll
-      for (int q = 0; q < NMF; ++q) mfma_one(q, a[ks & 1], b[ks & 1]);
+        for (int q = 0; q < NMF; ++q) mfma_one(q, a[ks & 1], b[ks & 1]);
+      });
+#pragma unroll
+      for (int q = 0; q < PRE; ++q) mfma_one(q, a[LB], b[LB]);
+      // Issue order: the next k-step's reads go out one per MFMA over the
+      // first MFMAs, so the remaining ones cover their latency.
+#pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) sched_run<NMF, NR, 0>();
     }
-#pragma unroll
-    for (int q = 0; q < PRE; ++q) mfma_one(q, a[LB], b[LB]);
-    // Issue order: the next k-step's reads go out one per MFMA over the first
-    // MFMAs, so the remaining ones cover their latency.
-#pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) sched_run<NMF, NR, 0>();
   };
-  frags(smem, 0, a[0], b[0]);
+  frags(smem, std::integral_constant<int, 0>{}, a[0], b[0]);
   for (int kt = 0; kt < nk - 1; ++kt) {
     slice_head(kt);
     // (sched_barrier: nothing may be moved across the wait and the barrier,
@@ -254,8 +368,16 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(min(kt + C::NS, nk - 1), kt % C::NS);
-    frags(smem + ((kt + 1) % C::NS) * C::STAGE, 0, a[0], b[0]);
+    if constexpr (BROW) {
+      const uint8_t* nx = smem + ((kt + 1) % C::NS) * C::STAGE;
+      frags_b(nx, std::integral_constant<int, 0>{}, b[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(kt + C::NS, nk - 1), kt % C::NS);
+      frags_a(nx, std::integral_constant<int, 0>{}, a[0]);
+    } else {
+      issue(min(kt + C::NS, nk - 1), kt % C::NS);
+      frags(smem + ((kt + 1) % C::NS) * C::STAGE, std::integral_constant<int, 0>{}, a[0], b[0]);
+    }
 #pragma unroll
     for (int q = PRE; q < NMF; ++q) mfma_one(q, a[LB], b[LB]);
     // Reads of the next slice's first k-step first, then the new group's
@@ -814,9 +936,11 @@ int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + 
 #ifndef MHA_GEMM_BIG_MIN_TILES
 #define MHA_GEMM_BIG_MIN_TILES 256
 #endif
-// Operands small enough for buffer-addressed copies (32-bit byte offsets).
-bool buf_ok(int M, int N, int K) {
-  return (long long)M * K * 2 <= 0x7fffffffLL && (long long)N * K * 2 <= 0x7fffffffLL;
+// Operands small enough for buffer-addressed copies (32-bit byte offsets):
+// A is M x K, the second operand `b_elems` 16-bit values (N x K, or K rows of
+// stride ldb).
+bool buf_ok(int M, int K, long long b_elems) {
+  return (long long)M * K * 2 <= 0x7fffffffLL && b_elems * 2 <= 0x7fffffffLL;
 }
 bool use_big(int M, int N) {
   return tiles_of(M, N, BigCfg::BM, BigCfg::BN) >= MHA_GEMM_BIG_MIN_TILES;
@@ -827,32 +951,35 @@ bool use_big(int M, int N) {
 using namespace gemm_impl;
 
 namespace {
+// The projection weights are read as they are given, row-major (K x N, row
+// stride ldw), through the transposing fragment reads.
 template <bool TRANS, typename Epi>
-hipError_t launch_qkv_part(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
+hipError_t launch_qkv_part(const uint16_t* A, int M, int K, const uint16_t* W, int ldw, int N,
                            const Epi& epi, hipStream_t s) {
   if (use_big(M, N)) {
-    if (buf_ok(M, N, K)) {
-      hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi, true>),
+    if (buf_ok(M, K, (long long)K * ldw)) {
+      hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi, true, true>),
                          dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
-                         Bt, M, N, K, epi);
+                         W, M, N, K, ldw, epi);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi, false>),
+    hipLaunchKernelGGL((gemm16_kernel<BigCfg, BF16, TRANS, Epi, false, true>),
                        dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
-                       Bt, M, N, K, epi);
+                       W, M, N, K, ldw, epi);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi, false>),
+  hipLaunchKernelGGL((gemm16_kernel<SmallCfg, BF16, TRANS, Epi, false, true>),
                      dim3(tiles_of(M, N, SmallCfg::BM, SmallCfg::BN)), dim3(SmallCfg::NT), 0, s, A,
-                     Bt, M, N, K, epi);
+                     W, M, N, K, ldw, epi);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
+hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* W, int ldw, int N,
                            const QkvEpilogue& e, hipStream_t s) {
-  // Columns [n_base, n_base + N) of [Q|K|V]: the Q and K part runs with
-  // transposed tiles, the V part with normal tiles.
+  // Columns [n_base, n_base + N) of [Q|K|V] (W points at column n_base): the
+  // Q and K part runs with transposed tiles, the V part with normal tiles.
+  if (N % 8 != 0 || ldw % 8 != 0 || K % 64 != 0) return hipErrorInvalidValue;
   const int n_lo = e.n_base, n_hi = e.n_base + N, split = e.D + e.Dkv;
   if (n_lo < split) {
     // With grouped key/value heads the K block is narrower than Q: Q and K
@@ -861,13 +988,13 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
     // large tiles).
     const int cut = (e.Dkv < e.D && n_lo < e.D && min(n_hi, split) > e.D) ? e.D : min(n_hi, split);
     QkEpi epi{e};
-    hipError_t err = launch_qkv_part<true>(A, M, K, Bt, cut - n_lo, epi, s);
+    hipError_t err = launch_qkv_part<true>(A, M, K, W, ldw, cut - n_lo, epi, s);
     if (err != hipSuccess) return err;
     if (cut < min(n_hi, split)) {
       QkEpi epi_k{e};
       epi_k.e.n_base = cut;
-      err = launch_qkv_part<true>(A, M, K, Bt + (size_t)(cut - n_lo) * K, min(n_hi, split) - cut,
-                                  epi_k, s);
+      err = launch_qkv_part<true>(A, M, K, W + (cut - n_lo), ldw, min(n_hi, split) - cut, epi_k,
+                                  s);
       if (err != hipSuccess) return err;
     }
   }
@@ -875,7 +1002,7 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, 
     const int v_lo = max(n_lo, split);
     VEpi epi{e};
     epi.e.n_base = v_lo;
-    return launch_qkv_part<false>(A, M, K, Bt + (size_t)(v_lo - n_lo) * K, n_hi - v_lo, epi, s);
+    return launch_qkv_part<false>(A, M, K, W + (v_lo - n_lo), ldw, n_hi - v_lo, epi, s);
   }
   return hipSuccess;
 }
@@ -897,18 +1024,18 @@ hipError_t launch_out_variant(const uint16_t* A, int M, int K, const uint16_t* B
                               const uint16_t* bias, const OutOptions& opt, hipStream_t s) {
   OutEpi<RESID, YBF16> epi{bias, opt.y, opt.resid};
   if (use_big(M, N))
-    if (buf_ok(M, N, K))
-      hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>, true>),
+    if (buf_ok(M, K, (long long)N * K))
+      hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>, true, false>),
                          dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
-                         Bt, M, N, K, epi);
+                         Bt, M, N, K, K, epi);
     else
-    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>, false>),
+    hipLaunchKernelGGL((gemm16_kernel<BigCfg, F16, true, OutEpi<RESID, YBF16>, false, false>),
                        dim3(tiles_of(M, N, BigCfg::BM, BigCfg::BN)), dim3(BigCfg::NT), 0, s, A,
-                       Bt, M, N, K, epi);
+                       Bt, M, N, K, K, epi);
   else
-    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, true, OutEpi<RESID, YBF16>, false>),
+    hipLaunchKernelGGL((gemm16_kernel<SmallCfg, F16, true, OutEpi<RESID, YBF16>, false, false>),
                        dim3(tiles_of(M, N, SmallCfg::BM, SmallCfg::BN)), dim3(SmallCfg::NT), 0,
-                       s, A, Bt, M, N, K, epi);
+                       s, A, Bt, M, N, K, K, epi);
   return hipGetLastError();
 }
 }  // namespace

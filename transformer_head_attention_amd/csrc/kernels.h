@@ -64,8 +64,9 @@ struct QkvEpilogue {
   float q_scale;         // multiplies the fp16 Q (the fp32 early copy is unscaled)
   int* overflow;         // set to 1 if a stored fp16 value is not finite, or null
 };
-// A: (M x K) bf16, Bt: (N x K) bf16.
-hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* Bt, int N,
+// A: (M x K) bf16; W: column n_base of the (K x N_qkv) bf16 weights, row
+// stride ldw (N, ldw multiples of 8, K of 64).
+hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* W, int ldw, int N,
                            const QkvEpilogue& e, hipStream_t s);
 // Where and how the output projection stores Y.
 struct OutOptions {

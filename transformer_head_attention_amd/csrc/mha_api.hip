@@ -55,7 +55,7 @@ int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
 struct Layout {
   // byte offsets into the workspace
-  size_t wqkvT = 0, woT = 0, q = 0, k = 0, vt = 0, o = 0, kend = 0, order = 0, mbits = 0, eqkv = 0,
+  size_t woT = 0, q = 0, k = 0, vt = 0, o = 0, kend = 0, order = 0, mbits = 0, eqkv = 0,
          eo = 0, wgT = 0, gate = 0;
   size_t f_q = 0, f_kv = 0, f_o = 0;
   size_t total = 0;
@@ -77,7 +77,6 @@ Layout make_layout(const mha_handle* hd, int B, int T_q, int T_k) {
     L.Tkp = round_up(T_k, bm);
     L.R = std::min(mha::kEarlyRows, T_q);
     const size_t Dkv = (size_t)hd->Dkv, Nqkv = (size_t)hd->Nqkv;
-    L.wqkvT = take(Nqkv * D * 2);
     L.woT = take(D * D * 2);
     L.q = take((size_t)B * L.Tqp * D * 2);
     L.k = take((size_t)B * L.Tkp * Dkv * 2);
@@ -410,7 +409,6 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
   if (hd->dtype == MHA_BF16) {
     const uint16_t* xq = static_cast<const uint16_t*>(x_q);
     const uint16_t* xkv = static_cast<const uint16_t*>(x_kv);
-    uint16_t* wqkvT = reinterpret_cast<uint16_t*>(ws + L.wqkvT);
     uint16_t* woT = reinterpret_cast<uint16_t*>(ws + L.woT);
     uint16_t* q = reinterpret_cast<uint16_t*>(ws + L.q);
     uint16_t* k = reinterpret_cast<uint16_t*>(ws + L.k);
@@ -425,15 +423,16 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     float* eqkv = reinterpret_cast<float*>(ws + L.eqkv);
     float* eo = reinterpret_cast<float*>(ws + L.eo);
     const uint16_t* bq = static_cast<const uint16_t*>(b_qkv);
+    const uint16_t* wq = static_cast<const uint16_t*>(w_qkv);
 
     // prep
-    // both weight transposes and the mask scan in one launch
+    // W_O's transposed fp16 copy, the gate weights' transpose and the mask
+    // scan in one launch (W_QKV is read as given)
     uint16_t* wgT = reinterpret_cast<uint16_t*>(ws + L.wgT);
-    const mha::TransposeJob tq{static_cast<const uint16_t*>(w_qkv), wqkvT, D, Nqkv, 0};
     const mha::TransposeJob to{static_cast<const uint16_t*>(w_o), woT, D, D, 1, f16_overflow};
     const mha::SmallTranspose tg{static_cast<const uint16_t*>(gate_w), wgT, D, h};
     const mha::MaskScan ms{key_padding_mask, B, T_k, kend, mbits};
-    MHA_HIP(mha::launch_prep(tq, &to, tg, ms, s));
+    MHA_HIP(mha::launch_prep(to, nullptr, tg, ms, s));
     if (ordered) MHA_HIP(mha::launch_mask_order(kend, B, order, s));
     if (!mark(1)) return MHA_ERR_HIP;
 
@@ -464,14 +463,14 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     if (!cross) {
       e.T = T_q;
       e.n_base = 0;
-      MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wqkvT, Nqkv, e, s));
+      MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wq, Nqkv, Nqkv, e, s));
     } else {
       e.T = T_q;
       e.n_base = 0;
-      MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wqkvT, D, e, s));
+      MHA_HIP(mha::launch_gemm_qkv(xq, B * T_q, D, wq, Nqkv, D, e, s));
       e.T = T_k;
       e.n_base = D;
-      MHA_HIP(mha::launch_gemm_qkv(xkv, B * T_k, D, wqkvT + (size_t)D * D, 2 * Dkv, e, s));
+      MHA_HIP(mha::launch_gemm_qkv(xkv, B * T_k, D, wq + D, Nqkv, 2 * Dkv, e, s));
     }
     if (!mark(2)) return MHA_ERR_HIP;
 

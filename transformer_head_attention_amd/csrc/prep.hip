@@ -1,7 +1,8 @@
-// Preparation kernels: weight transpose (+ bf16 -> fp16 conversion) so that
-// both MFMA operands of the projections are K-contiguous, and the scan of a
-// padding mask (key extent and per-tile ignore bits of each batch element),
-// in one launch; then the batch elements ranked by key extent.
+// Preparation kernels: W_O transposed and converted to fp16 for the output
+// projection (both of its MFMA operands K-contiguous fp16), the gate weights'
+// small transpose, and the scan of a padding mask (key extent and per-tile
+// ignore bits of each batch element), in one launch; then the batch elements
+// ranked by key extent.
 #include "device_common.h"
 #include "kernels.h"
 
