@@ -117,22 +117,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the projection weights are, instead of N x K: its K slices are copied as
 // BK rows of BN columns and the MFMA fragments (8 consecutive k of one
 // column per lane) are read with the transposing LDS read.
-template <typename C, typename Tag, bool TRANS, typename Epi, bool BUF, bool BROW>
-__global__ void __launch_bounds__(C::NT, C::OCC)
-gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, int M, int N,
-              int K, int ldb, Epi epi) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NS * C::STAGE];
-  // wave index in a scalar register: the DMA LDS bases below stay scalar
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-
-  // Tile order: each XCD takes a contiguous range of logical tiles, walked in
-  // groups of GM row bands so that the concurrently resident workgroups of
-  // an XCD share A rows and B columns in its L2.
+// Tile order: each XCD takes a contiguous range of logical tiles, walked in
+// groups of GM row bands so that the concurrently resident workgroups of an
+// XCD share A rows and B columns in its L2. (m0, n0): this workgroup's tile.
 #ifndef MHA_GEMM_GM
 #define MHA_GEMM_GM 8
 #endif
+template <typename C>
+__device__ __forceinline__ void tile_origin(int M, int N, int& m0, int& n0) {
   constexpr int GM = MHA_GEMM_GM;
   const int ntn = (N + C::BN - 1) / C::BN, ntm = (M + C::BM - 1) / C::BM;
   const int logical = xcd_remap(blockIdx.x, ntn * ntm);
@@ -140,7 +132,20 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   const int gm0 = group * GM, gsz = min(GM, ntm - gm0);
   const int in_group = logical - group * GM * ntn;
   const int bm = gm0 + in_group % gsz, bn = in_group / gsz;
-  const int m0 = bm * C::BM, n0 = bn * C::BN;
+  m0 = bm * C::BM;
+  n0 = bn * C::BN;
+}
+
+// One output tile at (m0, n0), with the workgroup's LDS `smem` (NS * STAGE bytes).
+template <typename C, typename Tag, bool TRANS, typename Epi, bool BUF, bool BROW>
+__device__ __forceinline__ void gemm16_tile(const uint16_t* __restrict__ A,
+                                            const uint16_t* __restrict__ Bt, int M, int N, int K,
+                                            int ldb, const Epi& epi, int m0, int n0,
+                                            uint8_t* smem) {
+  // wave index in a scalar register: the DMA LDS bases below stay scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   // DMA of K slice kt into stage `stage`: lane chunk p of a wave-wide load
   // lands at byte 16*p of the wave's 1 KiB window and fetches the global
@@ -395,6 +400,16 @@ gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, i
   static_assert(C::WM * C::WN * 2 <= C::NS * C::STAGE / C::NWAVES, "staging window");
   epi.template apply<C::TM, C::TN>(acc, m0 + wm * C::WM, n0 + wn * C::WN, lane, M, N,
                                    smem + wave * (C::NS * C::STAGE / C::NWAVES));
+}
+
+template <typename C, typename Tag, bool TRANS, typename Epi, bool BUF, bool BROW>
+__global__ void __launch_bounds__(C::NT, C::OCC)
+gemm16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, int M, int N,
+              int K, int ldb, Epi epi) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NS * C::STAGE];
+  int m0, n0;
+  tile_origin<C>(M, N, m0, n0);
+  gemm16_tile<C, Tag, TRANS, Epi, BUF, BROW>(A, Bt, M, N, K, ldb, epi, m0, n0, smem);
 }
 
 // Output staging: 16-byte chunk c of LDS row `row` (RB bytes per row) sits at
@@ -905,6 +920,24 @@ early_out_kernel(const float* __restrict__ O32, int M, int K, const uint16_t* __
   }
 }
 
+// The whole [Q|K|V] (or [K|V]) column range of the projection in one launch
+// of 256 x 256 tiles: a workgroup whose tile lies in the V block (columns
+// n >= vcol) runs the V path (normal tiles, V^T epilogue), the others the
+// Q/K path (transposed tiles). One launch instead of two lets each row band's
+// tiles of all three blocks run together, and saves a launch boundary.
+template <typename C, bool BUF>
+__global__ void __launch_bounds__(C::NT, C::OCC)
+gemm16_qkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N,
+                  int K, int ldw, QkEpi qk, VEpi ve, int vcol) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NS * C::STAGE];
+  int m0, n0;
+  tile_origin<C>(M, N, m0, n0);
+  if (n0 >= vcol)
+    gemm16_tile<C, BF16, false, VEpi, BUF, true>(A, W, M, N, K, ldw, ve, m0, n0, smem);
+  else
+    gemm16_tile<C, BF16, true, QkEpi, BUF, true>(A, W, M, N, K, ldw, qk, m0, n0, smem);
+}
+
 // Large problems: 256 x 256 tiles (below). Problems with too few such tiles
 // to fill the 256 CUs use 128 x 128 tiles, four waves of 64 x 64 (two
 // workgroups per CU).
@@ -981,6 +1014,22 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* W, i
   // Q and K part runs with transposed tiles, the V part with normal tiles.
   if (N % 8 != 0 || ldw % 8 != 0 || K % 64 != 0) return hipErrorInvalidValue;
   const int n_lo = e.n_base, n_hi = e.n_base + N, split = e.D + e.Dkv;
+  // One launch for both parts when the V block starts on a tile boundary,
+  // the launch fills the CUs with 256 x 256 tiles, and no narrower K block
+  // needs a launch of its own (grouped heads, below).
+  if (n_lo < split && n_hi > split && (split - n_lo) % BigCfg::BN == 0 && use_big(M, N) &&
+      !(e.Dkv < e.D && n_lo < e.D)) {
+    QkEpi qk{e};
+    VEpi ve{e};
+    const dim3 grid(tiles_of(M, N, BigCfg::BM, BigCfg::BN));
+    if (buf_ok(M, K, (long long)K * ldw))
+      hipLaunchKernelGGL((gemm16_qkv_kernel<BigCfg, true>), grid, dim3(BigCfg::NT), 0, s, A, W, M,
+                         N, K, ldw, qk, ve, split - n_lo);
+    else
+      hipLaunchKernelGGL((gemm16_qkv_kernel<BigCfg, false>), grid, dim3(BigCfg::NT), 0, s, A, W, M,
+                         N, K, ldw, qk, ve, split - n_lo);
+    return hipGetLastError();
+  }
   if (n_lo < split) {
     // With grouped key/value heads the K block is narrower than Q: Q and K
     // run as separate launches so that each picks its own tile size (one
