@@ -1014,41 +1014,43 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* W, i
   // Q and K part runs with transposed tiles, the V part with normal tiles.
   if (N % 8 != 0 || ldw % 8 != 0 || K % 64 != 0) return hipErrorInvalidValue;
   const int n_lo = e.n_base, n_hi = e.n_base + N, split = e.D + e.Dkv;
-  // One launch for both parts when the V block starts on a tile boundary,
-  // the launch fills the CUs with 256 x 256 tiles, and no narrower K block
-  // needs a launch of its own (grouped heads, below).
-  if (n_lo < split && n_hi > split && (split - n_lo) % BigCfg::BN == 0 && use_big(M, N) &&
-      !(e.Dkv < e.D && n_lo < e.D)) {
+  // With grouped key/value heads the K block is narrower than Q: Q runs as a
+  // launch of its own, so that Q and the rest each pick their tile size (one
+  // launch over D + Dkv columns would leave a mostly empty last round of
+  // large tiles).
+  int lo = n_lo;
+  if (e.Dkv < e.D && n_lo < e.D && n_hi > e.D) {
+    QkEpi epi{e};
+    const hipError_t err = launch_qkv_part<true>(A, M, K, W, ldw, e.D - n_lo, epi, s);
+    if (err != hipSuccess) return err;
+    lo = e.D;
+  }
+  const uint16_t* Wl = W + (lo - n_lo);
+  const int Nl = n_hi - lo;
+  // One launch for both parts when the V block starts on a tile boundary and
+  // the launch fills the CUs with 256 x 256 tiles.
+  if (lo < split && n_hi > split && (split - lo) % BigCfg::BN == 0 && use_big(M, Nl)) {
     QkEpi qk{e};
+    qk.e.n_base = lo;
     VEpi ve{e};
-    const dim3 grid(tiles_of(M, N, BigCfg::BM, BigCfg::BN));
+    ve.e.n_base = lo;
+    const dim3 grid(tiles_of(M, Nl, BigCfg::BM, BigCfg::BN));
     if (buf_ok(M, K, (long long)K * ldw))
-      hipLaunchKernelGGL((gemm16_qkv_kernel<BigCfg, true>), grid, dim3(BigCfg::NT), 0, s, A, W, M,
-                         N, K, ldw, qk, ve, split - n_lo);
+      hipLaunchKernelGGL((gemm16_qkv_kernel<BigCfg, true>), grid, dim3(BigCfg::NT), 0, s, A, Wl, M,
+                         Nl, K, ldw, qk, ve, split - lo);
     else
-      hipLaunchKernelGGL((gemm16_qkv_kernel<BigCfg, false>), grid, dim3(BigCfg::NT), 0, s, A, W, M,
-                         N, K, ldw, qk, ve, split - n_lo);
+      hipLaunchKernelGGL((gemm16_qkv_kernel<BigCfg, false>), grid, dim3(BigCfg::NT), 0, s, A, Wl,
+                         M, Nl, K, ldw, qk, ve, split - lo);
     return hipGetLastError();
   }
-  if (n_lo < split) {
-    // With grouped key/value heads the K block is narrower than Q: Q and K
-    // run as separate launches so that each picks its own tile size (one
-    // launch over D + Dkv columns would leave a mostly empty last round of
-    // large tiles).
-    const int cut = (e.Dkv < e.D && n_lo < e.D && min(n_hi, split) > e.D) ? e.D : min(n_hi, split);
+  if (lo < split) {
     QkEpi epi{e};
-    hipError_t err = launch_qkv_part<true>(A, M, K, W, ldw, cut - n_lo, epi, s);
+    epi.e.n_base = lo;
+    const hipError_t err = launch_qkv_part<true>(A, M, K, Wl, ldw, min(n_hi, split) - lo, epi, s);
     if (err != hipSuccess) return err;
-    if (cut < min(n_hi, split)) {
-      QkEpi epi_k{e};
-      epi_k.e.n_base = cut;
-      err = launch_qkv_part<true>(A, M, K, W + (cut - n_lo), ldw, min(n_hi, split) - cut, epi_k,
-                                  s);
-      if (err != hipSuccess) return err;
-    }
   }
   if (n_hi > split) {
-    const int v_lo = max(n_lo, split);
+    const int v_lo = max(lo, split);
     VEpi epi{e};
     epi.e.n_base = v_lo;
     return launch_qkv_part<false>(A, M, K, W + (v_lo - n_lo), ldw, n_hi - v_lo, epi, s);
