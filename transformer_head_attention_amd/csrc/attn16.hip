@@ -49,6 +49,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "transpose_tile.h"
 
 namespace mha {
 
@@ -252,9 +253,10 @@ __device__ __forceinline__ void map_block(const AttnF16Args& a, int L, int nqb, 
 
 // d_k = 128: the register budget is capped at two waves per SIMD (247 VGPRs,
 // no spill); with two pipeline stages (64 KiB of LDS) two workgroups then
-// share a CU.
+// share a CU. d_k = 64: capped at three waves per SIMD (168 VGPRs; the W_O
+// conversion path alone would let the compiler take a few more).
 template <int DK, int NQ, int NS, bool HAS_MASK>
-__global__ void __launch_bounds__(NT, (DK == 128 ? 2 : 1))
+__global__ void __launch_bounds__(NT, (DK == 128 ? 2 : 3))
 attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   constexpr int BLOCK_M = NWAVES * 32 * NQ;
   constexpr int KCH = DK / 8;                       // 16-byte chunks per K row
@@ -273,11 +275,20 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE + 32];
   uint32_t (*mask_s)[2] = reinterpret_cast<uint32_t (*)[2]>(smem + NS * STAGE);
 
-  // The first early_slots workgroups evaluate the early causal rows.
-  if ((int)blockIdx.x < early_slots) {
+  // The first wo_slots workgroups convert W_O for the output projection (a
+  // multiple of 8, so the XCD of every later workgroup is unchanged), the
+  // next early_slots evaluate the early causal rows.
+  if ((int)blockIdx.x < a.wo_slots) {
+    static_assert(NS * STAGE >= kTransposeTile * (kTransposeTile + 8) * 2, "tile fits the stages");
+    if ((int)blockIdx.x < transpose_tiles(a.wo))
+      transpose_tile64(a.wo, (int)blockIdx.x,
+                       reinterpret_cast<uint16_t(*)[kTransposeTile + 8]>(smem));
+    return;
+  }
+  const int bid = (int)blockIdx.x - a.wo_slots;
+  if (bid < early_slots) {
     static_assert(NS * STAGE >= 2 * 64 * DK * 4, "early-row staging fits the stages");
-    if ((long long)blockIdx.x < early_blocks(early, ER))
-      early_rows_block<DK, NWAVES>(early, (int)blockIdx.x, smem);
+    if ((long long)bid < early_blocks(early, ER)) early_rows_block<DK, NWAVES>(early, bid, smem);
     return;
   }
   // wave index in a scalar register: the query rows of the wave, the DMA LDS
@@ -288,7 +299,7 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
 
   const int nqb = (a.T_q + BLOCK_M - 1) / BLOCK_M;
   int b, head, qblk;
-  map_block<HAS_MASK>(a, (int)blockIdx.x - early_slots, nqb, b, head, qblk);
+  map_block<HAS_MASK>(a, bid - early_slots, nqb, b, head, qblk);
   const int bh = b * a.h + head;
   // Key/value set of this query head: consecutive heads share one set, and
   // their workgroups are consecutive in the XCD mappings above, so a set's K
@@ -626,12 +637,13 @@ constexpr int nq_for(int d_k) { return d_k == 64 ? MHA_ATTN_NQ64 : 1; }
 template <int DK, int NS>
 hipError_t launch_dk(const AttnF16Args& a, int total, const AttnF32Args& e, int extra,
                      hipStream_t s) {
+  const unsigned grid = (unsigned)(a.wo_slots + extra + total);
   if (a.mbits)
-    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, true>), dim3(total + extra), dim3(NT),
-                       0, s, a, e, extra);
+    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, true>), dim3(grid), dim3(NT), 0, s, a,
+                       e, extra);
   else
-    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, false>), dim3(total + extra),
-                       dim3(NT), 0, s, a, e, extra);
+    hipLaunchKernelGGL((attn_f16_kernel<DK, nq_for(DK), NS, false>), dim3(grid), dim3(NT), 0, s,
+                       a, e, extra);
   return hipGetLastError();
 }
 
@@ -675,7 +687,13 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
            2LL * ag.group_units <= per_xcd)
       ag.group_units *= 2;
   }
-  if ((long long)total + extra > 0x7fffffffLL) return hipErrorInvalidValue;
+  ag.wo_slots = 0;
+  if (a.wo.W) {
+    if (a.wo.K < 1 || a.wo.N < 1 || a.wo.K % 8 != 0 || a.wo.N % 8 != 0 || !a.wo.WT)
+      return hipErrorInvalidValue;
+    ag.wo_slots = (transpose_tiles(a.wo) + 7) / 8 * 8;
+  }
+  if ((long long)total + extra + ag.wo_slots > 0x7fffffffLL) return hipErrorInvalidValue;
   if (d_k == 64) return launch_dk<64, MHA_ATTN_NS64>(ag, total, e, extra, s);
   if (d_k == 128) return launch_dk<128, MHA_ATTN_NS128>(ag, total, e, extra, s);
   return hipErrorInvalidValue;

@@ -100,7 +100,11 @@ struct AttnF16Args {
   const float* gate;   // (B*T_q, h) gate pre-activations g (row b*T_q + t): head i's output
                        // row t is multiplied by 1 / (1 + exp(-g)); null: no gate
   int B, h, h_kv, T_q, T_k, Tqp, Tkp, D, causal;
+  // W_O -> W_O^T in fp16 for the output projection, by extra workgroups at
+  // the start of the launch (independent of the attention; W null: none)
+  TransposeJob wo;
   int group_units;     // set by launch_attn_f16 (causal query-block interleave)
+  int wo_slots;        // set by launch_attn_f16: workgroups of the W_O job
 };
 int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp, Tkp must be multiples)
 int attn_mask_tiles(int T_k);    // 64-key tiles covering T_k

@@ -154,6 +154,9 @@ mha_status_t check_forward_args(const mha_handle* hd, const void* x_q, const voi
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
+// Largest d_model whose W_O conversion runs inside the attention launch.
+constexpr int kWoInAttentionMaxD = 2048;
+
 // Scratch of mha_forward_noalloc: one copy per GPU, loaded with the code
 // object. Host code never passes `scratch` itself (on the host it only names
 // the symbol): each device's address is looked up once, with that device
@@ -425,14 +428,19 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     const uint16_t* bq = static_cast<const uint16_t*>(b_qkv);
     const uint16_t* wq = static_cast<const uint16_t*>(w_qkv);
 
-    // prep
-    // W_O's transposed fp16 copy, the gate weights' transpose and the mask
-    // scan in one launch (W_QKV is read as given)
+    // prep: W_O's transposed fp16 copy for the output projection, the gate
+    // weights' transpose and the mask scan, in one launch (W_QKV is read as
+    // given). With neither mask nor gate and D <= kWoInAttentionMaxD, W_O is
+    // converted by the attention launch's first workgroups instead and there
+    // is no prep launch: at D = 512 and 1024 that saves the launch; at D =
+    // 4096 the 32 MiB conversion slowed the attention by more than it cost
+    // here.
     uint16_t* wgT = reinterpret_cast<uint16_t*>(ws + L.wgT);
     const mha::TransposeJob to{static_cast<const uint16_t*>(w_o), woT, D, D, 1, f16_overflow};
     const mha::SmallTranspose tg{static_cast<const uint16_t*>(gate_w), wgT, D, h};
     const mha::MaskScan ms{key_padding_mask, B, T_k, kend, mbits};
-    MHA_HIP(mha::launch_prep(to, nullptr, tg, ms, s));
+    const bool wo_in_attention = !key_padding_mask && !gate_w && D <= kWoInAttentionMaxD;
+    if (!wo_in_attention) MHA_HIP(mha::launch_prep(to, nullptr, tg, ms, s));
     if (ordered) MHA_HIP(mha::launch_mask_order(kend, B, order, s));
     if (!mark(1)) return MHA_ERR_HIP;
 
@@ -494,6 +502,7 @@ mha_status_t mha_forward_ex(mha_handle_t hd, const void* x_q, const void* x_kv, 
     a.Tkp = L.Tkp;
     a.D = D;
     a.causal = causal;
+    if (wo_in_attention) a.wo = to;
     // Early causal rows, re-evaluated in fp32 by workgroups appended to the
     // attention launch (their output projection follows out_proj).
     mha::AttnF32Args f{};

@@ -5,23 +5,20 @@
 // ranked by key extent.
 #include "device_common.h"
 #include "kernels.h"
+#include "transpose_tile.h"
 
 namespace mha {
 
 namespace {
 
-constexpr int TT = 64;   // transpose tile edge
+constexpr int TT = kTransposeTile;
 
 // One launch: workgroups [0, tiles_t) transpose weights, WT[n][k] = W[k][n]
 // for up to two matrices (the first `tiles0` workgroups take the first), one
 // 64 x 64 tile each; workgroups [tiles_t, small_end) transpose a small matrix
 // (the gate weights) one element per thread; workgroups past them scan the
-// padding mask of one batch element each.
-//
-// Transpose: global traffic moves 16 bytes per lane both ways: rows of W are
-// read as 8-element chunks, and each output chunk gathers 8 consecutive k of
-// one column from LDS (rows padded by 16 bytes, so the 8 lanes gathering one
-// column chunk hit different banks). Requires K and N to be multiples of 8.
+// padding mask of one batch element each (the transpose tile itself:
+// transpose_tile64).
 //
 // Mask scan: each wave takes 64-key tiles in turn, one key per lane; the
 // wave's ballot of "ignored" (masked or past T_k) is the tile's 64-bit ignore
@@ -64,42 +61,7 @@ prep_kernel(TransposeJob j0, TransposeJob j1, int tiles0, int tiles_t, SmallTran
     return;
   }
   const bool second = (int)blockIdx.x >= tiles0;
-  const TransposeJob& jb = second ? j1 : j0;
-  const int blk = second ? (int)blockIdx.x - tiles0 : (int)blockIdx.x;
-  const uint16_t* __restrict__ W = jb.W;
-  uint16_t* __restrict__ WT = jb.WT;
-  const int K = jb.K, N = jb.N;
-  const int ntx = (N + TT - 1) / TT;
-  const int n0 = (blk % ntx) * TT, k0 = (blk / ntx) * TT;
-  const int t = threadIdx.x, r = t >> 3, c = t & 7;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int kr = r + 32 * pass, k = k0 + kr, n = n0 + 8 * c;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (k < K && n < N) v = *reinterpret_cast<const u32x4*>(W + (size_t)k * N + n);
-    *reinterpret_cast<u32x4*>(&tile[kr][8 * c]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int nr = r + 32 * pass, n = n0 + nr, k = k0 + 8 * c;
-    if (n < N && k < K) {
-      uint16_t e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint16_t v = tile[8 * c + j][nr];
-        if (jb.to_f16) {
-          const float f = bf16_bits_to_float(v);
-          v = float_to_f16_bits(f);
-          flag_f16_overflow(jb.overflow, fabsf(f));
-        }
-        e[j] = v;
-      }
-      *reinterpret_cast<u32x4*>(WT + (size_t)n * K + k) =
-          u32x4{e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
-                e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16};
-    }
-  }
+  transpose_tile64(second ? j1 : j0, second ? (int)blockIdx.x - tiles0 : (int)blockIdx.x, tile);
 }
 
 // One workgroup per batch element: largest unmasked key index + 1.
@@ -120,17 +82,13 @@ mask_order_kernel(const int* __restrict__ kend, int B, int* __restrict__ order) 
 
 }  // namespace
 
-static int transpose_tiles(const TransposeJob& j) {
-  return ((j.N + TT - 1) / TT) * ((j.K + TT - 1) / TT);
-}
-
 hipError_t launch_prep(const TransposeJob& j0, const TransposeJob* j1, const SmallTranspose& st,
                        const MaskScan& ms, hipStream_t s) {
-  const long long t0 = transpose_tiles(j0), t1 = j1 ? transpose_tiles(*j1) : 0;
+  const long long t0 = j0.W ? transpose_tiles(j0) : 0, t1 = j1 && j1->W ? transpose_tiles(*j1) : 0;
   const long long ns = st.W ? ((long long)st.K * st.N + 255) / 256 : 0;
   const long long nb = ms.mask ? ms.B : 0;
-  if (t0 + t1 < 1 || t0 + t1 + ns + nb > 0x7fffffffLL || (ms.mask && ms.T_k < 1) ||
-      (st.W && (st.K < 1 || st.N < 1)))
+  if ((j1 && j1->W && !j0.W) || t0 + t1 + ns + nb < 1 || t0 + t1 + ns + nb > 0x7fffffffLL ||
+      (ms.mask && ms.T_k < 1) || (st.W && (st.K < 1 || st.N < 1)))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(t0 + t1 + ns + nb)), dim3(256), 0, s, j0,
                      j1 ? *j1 : j0, (int)t0, (int)(t0 + t1), st, (int)(t0 + t1 + ns), ms);
