@@ -57,7 +57,8 @@ PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "attention": ["transformer_head_attention_amd/csrc/attn16.hip",
-                  "transformer_head_attention_amd/csrc/device_common.h"],
+                  "transformer_head_attention_amd/csrc/device_common.h",
+                  "transformer_head_attention_amd/csrc/transpose_tile.h"],
     "decode_attention": ["transformer_head_attention_amd/csrc/decode.hip",
                          "transformer_head_attention_amd/csrc/device_common.h"],
     # the QKV projection's GEMM launches (their bytes are summed per step)
