@@ -964,8 +964,9 @@ using SmallCfg = Cfg<128, 128, 64, 64, MHA_SMALL_BK, MHA_SMALL_NS>;
 
 int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 // Big tiles once they fill at least one round of the 256 CUs (one workgroup
-// per CU): at D = 512 the Q|K launch (256 big tiles) takes 41 instead of 44
-// us that way; half a round (128 tiles) is slower than the small tiles.
+// per CU): a launch of 256 big tiles (the Q|K columns at D = 512, measured
+// when they ran as a launch of their own) took 41 instead of 44 us that way;
+// half a round (128 tiles) is slower than the small tiles.
 #ifndef MHA_GEMM_BIG_MIN_TILES
 #define MHA_GEMM_BIG_MIN_TILES 256
 #endif
