@@ -106,6 +106,13 @@ MID = [
                                                                             T_k=777)),
     ("bf16 non-causal self", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=2, T_q=257, T_k=257,
                                                                         causal=False)),
+    # enough 256 x 256 tiles for the single [Q|K|V] launch, with a ragged
+    # last row band (7000 rows) and a sequence boundary inside tiles
+    ("bf16 causal d1024 single QKV launch ragged", W["causal_bf16_d1024_h16_b8_t4096"],
+     dict(B=7, T_q=1000, T_k=1000)),
+    # the same for the cross-attention [K|V] launch (17000 rows of X_kv)
+    ("bf16 cross padded single [K|V] launch ragged", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
+     dict(B=17, T_q=90, T_k=1000, padding=(100, 1000))),
     ("bf16 cross padded ragged", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
      dict(B=3, T_q=200, T_k=333, padding=(40, 333))),
     ("bf16 causal d_k=128", W["causal_bf16_d4096_h32_b1_t8192"], dict(T_q=300, T_k=300)),
