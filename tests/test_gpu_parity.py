@@ -106,11 +106,15 @@ MID = [
                                                                             T_k=777)),
     ("bf16 non-causal self", W["causal_bf16_d1024_h16_b8_t4096"], dict(B=2, T_q=257, T_k=257,
                                                                         causal=False)),
-    # enough 256 x 256 tiles for the single [Q|K|V] launch, with a ragged
-    # last row band (7000 rows) and a sequence boundary inside tiles
-    ("bf16 causal d1024 single QKV launch ragged", W["causal_bf16_d1024_h16_b8_t4096"],
+    # the single [Q|K|V] launch with a ragged last row band and sequence
+    # boundaries inside tiles: 8400 rows give 396 tiles of 256 x 256 (a last
+    # round more than half full: those tiles); 7000 rows give 336 (a last
+    # round at most half full: 256 x 128 tiles, two workgroups per CU)
+    ("bf16 causal d1024 single QKV launch, big tiles, ragged", W["causal_bf16_d1024_h16_b8_t4096"],
+     dict(B=8, T_q=1050, T_k=1050)),
+    ("bf16 causal d1024 single QKV launch, mid tiles, ragged", W["causal_bf16_d1024_h16_b8_t4096"],
      dict(B=7, T_q=1000, T_k=1000)),
-    # the same for the cross-attention [K|V] launch (17000 rows of X_kv)
+    # the cross-attention [K|V] launch (17000 rows of X_kv: 268 big tiles)
     ("bf16 cross padded single [K|V] launch ragged", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],
      dict(B=17, T_q=90, T_k=1000, padding=(100, 1000))),
     ("bf16 cross padded ragged", W["cross_pad_bf16_d512_h8_b32_tq512_tk2048"],

@@ -961,6 +961,11 @@ gemm16_qkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W
 // D = 1024.)
 using BigCfg = Cfg<256, 256, 128, 64, MHA_BIG_BK, MHA_BIG_NS, 2>;
 using SmallCfg = Cfg<128, 128, 64, 64, MHA_SMALL_BK, MHA_SMALL_NS>;
+// 256 x 128 tiles over 8 waves of 64 x 64, 32-deep slices, 3 stages (72 KiB):
+// two workgroups per CU. For the single QKV launch when 256 x 256 tiles would
+// leave a last round at most half full (the D = 512 workload: 384 big tiles,
+// 1.5 rounds): its 768 tiles finish in about 1.2 big-tile rounds.
+using MidCfg = Cfg<256, 128, 64, 64, 32, 3, 2>;
 
 int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 // Big tiles once they fill at least one round of the 256 CUs (one workgroup
@@ -1035,6 +1040,17 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* W, i
     qk.e.n_base = lo;
     VEpi ve{e};
     ve.e.n_base = lo;
+    const int tb = tiles_of(M, Nl, BigCfg::BM, BigCfg::BN);
+    if (tb % 256 != 0 && tb % 256 <= 128 && tb < 4 * 256) {   // a ragged last round
+      const dim3 gm(tiles_of(M, Nl, MidCfg::BM, MidCfg::BN));
+      if (buf_ok(M, K, (long long)K * ldw))
+        hipLaunchKernelGGL((gemm16_qkv_kernel<MidCfg, true>), gm, dim3(MidCfg::NT), 0, s, A, Wl, M,
+                           Nl, K, ldw, qk, ve, split - lo);
+      else
+        hipLaunchKernelGGL((gemm16_qkv_kernel<MidCfg, false>), gm, dim3(MidCfg::NT), 0, s, A, Wl,
+                           M, Nl, K, ldw, qk, ve, split - lo);
+      return hipGetLastError();
+    }
     const dim3 grid(tiles_of(M, Nl, BigCfg::BM, BigCfg::BN));
     if (buf_ok(M, K, (long long)K * ldw))
       hipLaunchKernelGGL((gemm16_qkv_kernel<BigCfg, true>), grid, dim3(BigCfg::NT), 0, s, A, Wl, M,
