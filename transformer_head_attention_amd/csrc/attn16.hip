@@ -316,6 +316,13 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   if (HAS_MASK) kv_end = min(kv_end, a.kend[b]);
   if (a.causal) kv_end = min(kv_end, qblk * BLOCK_M + BLOCK_M);
   const int ntiles = kv_end > 0 ? (kv_end + BLOCK_N - 1) / BLOCK_N : 0;
+  if (a.prio_maxt > 0) {
+    // the launch is bound by its longest causal blocks: their waves issue
+    // first (priority 2 from two thirds of the longest, 1 from a third)
+    const int pr = (3 * ntiles) / a.prio_maxt;
+    if (pr >= 2) __builtin_amdgcn_s_setprio(2);
+    else if (pr >= 1) __builtin_amdgcn_s_setprio(1);
+  }
   const uint32_t* mbits_g = HAS_MASK ? a.mbits + (size_t)b * a.mbits_ld * 2 : nullptr;
 
   // Issue the DMA loads of key tile `tile` into LDS stage `stage`. Lane
@@ -686,6 +693,21 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
     while (ag.group_units < 16 && 2LL * ag.group_units * unit_kv <= MHA_ATTN_GROUP_BYTES &&
            2LL * ag.group_units <= per_xcd)
       ag.group_units *= 2;
+  }
+  // Causal, unpadded: when the average work per resident workgroup is less
+  // than 1.5 times the longest block's key tiles (short sequences, e.g. T =
+  // 1024 with 8 query blocks per head), that block's chain of tiles bounds
+  // the launch and its waves get issue priority; at T = 4096 (176 tiles per
+  // slot against 64) priority only cost time.
+  ag.prio_maxt = 0;
+  if (a.causal && !a.mbits) {
+    const long long maxt = (a.T_k + BLOCK_N - 1) / BLOCK_N;
+    const int nqb = (a.T_q + bm - 1) / bm;
+    long long tiles = 0;
+    for (int j = 0; j < nqb; ++j) tiles += (std::min(a.T_k, (j + 1) * bm) + BLOCK_N - 1) / BLOCK_N;
+    tiles *= (long long)a.h * a.B;
+    const long long slots = 256LL * (d_k == 128 ? 2 : 3);
+    if (2 * tiles < 3 * maxt * slots) ag.prio_maxt = (int)maxt;
   }
   ag.wo_slots = 0;
   if (a.wo.W) {

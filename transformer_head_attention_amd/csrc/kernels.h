@@ -105,6 +105,8 @@ struct AttnF16Args {
   TransposeJob wo;
   int group_units;     // set by launch_attn_f16 (causal query-block interleave)
   int wo_slots;        // set by launch_attn_f16: workgroups of the W_O job
+  int prio_maxt;       // set by launch_attn_f16: key tiles of the longest causal block when
+                       // those bound the launch (waves of long blocks get issue priority), else 0
 };
 int attn_f16_block_m(int d_k);   // query rows per workgroup (Tqp, Tkp must be multiples)
 int attn_mask_tiles(int T_k);    // 64-key tiles covering T_k
