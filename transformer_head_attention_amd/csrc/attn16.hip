@@ -701,11 +701,12 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
   // slot against 64) priority only cost time.
   ag.prio_maxt = 0;
   if (a.causal && !a.mbits) {
+    // block j < nqb - 1 of a head walks (j + 1) bm / BLOCK_N key tiles (bm is
+    // a multiple of BLOCK_N), the last one all maxt of them
+    static_assert(BLOCK_N == 64, "tile count below");
     const long long maxt = (a.T_k + BLOCK_N - 1) / BLOCK_N;
-    const int nqb = (a.T_q + bm - 1) / bm;
-    long long tiles = 0;
-    for (int j = 0; j < nqb; ++j) tiles += (std::min(a.T_k, (j + 1) * bm) + BLOCK_N - 1) / BLOCK_N;
-    tiles *= (long long)a.h * a.B;
+    const long long nqb = (a.T_q + bm - 1) / bm, per = bm / BLOCK_N;
+    const long long tiles = (per * (nqb - 1) * nqb / 2 + maxt) * a.h * a.B;
     const long long slots = 256LL * (d_k == 128 ? 2 : 3);
     if (2 * tiles < 3 * maxt * slots) ag.prio_maxt = (int)maxt;
   }
