@@ -683,14 +683,17 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
   const int total = ((a.T_q + bm - 1) / bm) * a.h * a.B;
   // Causal, unpadded: query blocks of groups of G units are interleaved
   // longest first. G keeps the group's K and V (4 Tkp d_k bytes per key/value
-  // set, shared by h / h_kv heads) within MHA_ATTN_GROUP_BYTES, at most 16 and
-  // at most the units one XCD runs.
+  // set, shared by h / h_kv heads) within MHA_ATTN_GROUP_BYTES (twice that
+  // at d_k = 128, whose two workgroups per CU leave each XCD fewer units in
+  // flight: at D = 4096, T = 8192 G = 4 instead of 2 took the attention from
+  // 0.541 to 0.535 ms), at most 16 and at most the units one XCD runs.
   AttnF16Args ag = a;
   ag.group_units = 1;
   if (a.causal && !a.mbits) {
     const long long unit_kv = 4LL * a.Tkp * d_k / (a.h / a.h_kv);
     const long long per_xcd = (long long)a.h * a.B / 8;
-    while (ag.group_units < 16 && 2LL * ag.group_units * unit_kv <= MHA_ATTN_GROUP_BYTES &&
+    const long long gbytes = d_k == 128 ? 2 * MHA_ATTN_GROUP_BYTES : MHA_ATTN_GROUP_BYTES;
+    while (ag.group_units < 16 && 2LL * ag.group_units * unit_kv <= gbytes &&
            2LL * ag.group_units <= per_xcd)
       ag.group_units *= 2;
   }
