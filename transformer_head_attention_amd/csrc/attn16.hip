@@ -102,20 +102,34 @@ __device__ __forceinline__ int swz(int row, int c) {
 // this come first in the attention grid (their count rounded up to a
 // multiple of 8, so the attention blocks keep their XCD placement); being
 // short, they leave room to the long causal blocks within microseconds,
-// which is cheaper than a launch of their own. A workgroup takes 16 query rows of one (batch, head); 16
-// lanes share a row, each owning d_k/16 dimensions; all (<= 64) keys of the
-// row sit in LDS as fp32 (rows past the extent zeroed, so the key loops have
-// no branches), the scores in registers: two plain passes (maximum, then
-// exponentials and the weighted sum of V), in log2 units.
-constexpr int ER = 16;   // query rows per early-row workgroup of 4 waves (4 rows per wave)
+// which is cheaper than a launch of their own. A workgroup takes 4 er_rpw
+// query rows of one (batch, head); 64 / er_rpw lanes share a row, each owning
+// as many dimensions; all (<= 64) keys of the row sit in LDS as fp32 (rows
+// past the extent zeroed, so the key loops have no branches), the scores in
+// registers: two plain passes (maximum, then exponentials and the weighted
+// sum of V), in log2 units.
+// Query rows per wave of an early-row workgroup (4 waves): 16 at d_k = 64 (one
+// workgroup per (batch element, head) for the 64 early rows, so each loads
+// that head's keys and values once: the D = 512 attention 37.0 -> 35.2 us), 4
+// at d_k = 128 (more rows per wave there made the D = 4096 attention slower).
+template <int DK>
+constexpr int er_rpw() { return DK == 64 ? 16 : 4; }
+template <int DK>
+constexpr int er_rows() { return 4 * er_rpw<DK>(); }   // query rows per early-row workgroup
 
 // Sum over the 16 lanes of a DPP row (every lane gets the total):
 // quad_perm xor 1, quad_perm xor 2, row_half_mirror, row_mirror.
-__device__ __forceinline__ float row16_sum(float v) {
+// Sum over LPR consecutive lanes (4, 8 or 16; every lane gets its group's
+// total): quad_perm xor 1, quad_perm xor 2, row_half_mirror, row_mirror.
+template <int LPR>
+__device__ __forceinline__ float lanes_sum(float v) {
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16, "lane group");
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  if constexpr (LPR >= 8)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  if constexpr (LPR >= 16)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
   return v;
 }
 
@@ -127,16 +141,18 @@ __host__ __device__ inline long long early_blocks(const AttnF32Args& e, int er) 
 // rows each; lds: at least 2 * 64 * DK * 4 bytes.
 template <int DK, int NWV>
 __device__ __forceinline__ void early_rows_block(const AttnF32Args& a, int blk, uint8_t* lds) {
-  constexpr int CPL = DK / 16;   // dimensions per lane
-  constexpr int ERW = NWV * 4;   // query rows per workgroup
+  constexpr int RPW = er_rpw<DK>();   // query rows per wave
+  constexpr int LPR = 64 / RPW;       // lanes per query row
+  constexpr int CPL = DK / LPR;       // dimensions per lane
+  constexpr int ERW = NWV * RPW;      // query rows per workgroup
   constexpr int NTW = NWV * 64;
   float (*Ks)[DK] = reinterpret_cast<float (*)[DK]>(lds);
   float (*Vs)[DK] = reinterpret_cast<float (*)[DK]>(lds + 64 * DK * 4);
   const int nx = (a.rows + ERW - 1) / ERW;
   const int bx = blk % nx, head = (blk / nx) % a.h, b = blk / (nx * a.h);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int p = lane & 15;
-  const int t = bx * ERW + wave * 4 + (lane >> 4);
+  const int p = lane % LPR;
+  const int t = bx * ERW + wave * RPW + lane / LPR;
   const bool valid = t < a.rows;
   const int kend = a.causal ? min(a.T_k, bx * ERW + ERW) : a.T_k;   // <= 64 (host-checked)
 
@@ -178,7 +194,7 @@ __device__ __forceinline__ void early_rows_block(const AttnF32Args& a, int blk, 
     float part = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) part = __builtin_fmaf(q[c], Ks[j][p * CPL + c], part);
-    part = row16_sum(part);
+    part = lanes_sum<LPR>(part);
     sc[j] = ((live >> j) & 1ull) ? part : -INFINITY;
     mx = fmaxf(mx, sc[j]);
   }
@@ -288,7 +304,8 @@ attn_f16_kernel(AttnF16Args a, AttnF32Args early, int early_slots) {
   const int bid = (int)blockIdx.x - a.wo_slots;
   if (bid < early_slots) {
     static_assert(NS * STAGE >= 2 * 64 * DK * 4, "early-row staging fits the stages");
-    if ((long long)bid < early_blocks(early, ER)) early_rows_block<DK, NWAVES>(early, bid, smem);
+    if ((long long)bid < early_blocks(early, er_rows<DK>()))
+      early_rows_block<DK, NWAVES>(early, bid, smem);
     return;
   }
   // wave index in a scalar register: the query rows of the wave, the DMA LDS
@@ -664,8 +681,8 @@ hipError_t launch_attn_f16(const AttnF16Args& a, int d_k, const AttnF32Args* ear
                            hipStream_t s) {
   if (a.h_kv < 1 || a.h % a.h_kv != 0) return hipErrorInvalidValue;
   const int bm = attn_f16_block_m(d_k);
-  // early rows per workgroup: 4 per wave
-  const int er = ER;
+  // early rows per workgroup
+  const int er = d_k == 64 ? er_rows<64>() : er_rows<128>();
   AttnF32Args e{};
   int extra = 0;
   if (early) {
