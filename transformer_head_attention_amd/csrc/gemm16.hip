@@ -938,6 +938,27 @@ gemm16_qkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W
     gemm16_tile<C, BF16, true, QkEpi, BUF, true>(A, W, M, N, K, ldw, qk, m0, n0, smem);
 }
 
+// Key/value sets of 64 columns (d_k = 64) on their own, as one key/value set
+// shared by every query head (MQA) gives: the K and V blocks are one wave
+// column each of a 128 x 128 tile, so the waves of the K half take the K
+// path (transposed tile, QkEpi) and those of the V half the V path (VEpi),
+// over the same staged slices and through the same barriers, instead of two
+// launches of half-empty tiles.
+template <typename C>
+__global__ void __launch_bounds__(C::NT, C::OCC)
+gemm16_kv64_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N,
+                   int K, int ldw, QkEpi qk, VEpi ve) {
+  static_assert(C::WN == 64 && C::BN == 2 * C::WN, "one wave column per block");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NS * C::STAGE];
+  int m0, n0;
+  tile_origin<C>(M, N, m0, n0);
+  const int wn = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) % C::WAVES_N);
+  if (wn == 0)
+    gemm16_tile<C, BF16, true, QkEpi, false, true>(A, W, M, N, K, ldw, qk, m0, n0, smem);
+  else
+    gemm16_tile<C, BF16, false, VEpi, false, true>(A, W, M, N, K, ldw, ve, m0, n0, smem);
+}
+
 // Large problems: 256 x 256 tiles (below). Problems with too few such tiles
 // to fill the 256 CUs use 128 x 128 tiles, four waves of 64 x 64 (two
 // workgroups per CU).
@@ -1058,6 +1079,17 @@ hipError_t launch_gemm_qkv(const uint16_t* A, int M, int K, const uint16_t* W, i
     else
       hipLaunchKernelGGL((gemm16_qkv_kernel<BigCfg, false>), grid, dim3(BigCfg::NT), 0, s, A, Wl,
                          M, Nl, K, ldw, qk, ve, split - lo);
+    return hipGetLastError();
+  }
+  // [K|V] of one 64-column key/value set each (MQA, d_k = 64): one launch
+  if (split - lo == SmallCfg::WN && n_hi - lo == SmallCfg::BN && !use_big(M, Nl)) {
+    QkEpi qk{e};
+    qk.e.n_base = lo;
+    VEpi ve{e};
+    ve.e.n_base = lo;
+    hipLaunchKernelGGL((gemm16_kv64_kernel<SmallCfg>),
+                       dim3(tiles_of(M, Nl, SmallCfg::BM, SmallCfg::BN)), dim3(SmallCfg::NT), 0, s,
+                       A, Wl, M, Nl, K, ldw, qk, ve);
     return hipGetLastError();
   }
   if (lo < split) {
